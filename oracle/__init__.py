@@ -1,0 +1,44 @@
+"""CPU oracle for the fp16 sum-reduction library -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything in this package.  The
+library itself never calls it, and the oracle never imports the library: the
+two share no code.  The only thing both sides see is the data, made by
+``synth_inputs``.
+
+Sources (cited by title and section throughout):
+
+* [TCR] "GPU Tensor Cores for fast Arithmetic Reductions", arXiv 2001.05585,
+  Abstract.  The operation is the arithmetic reduction (sum) of n numbers;
+  sub-results and the final result are 32-bit floats.
+* [TBB] "Taming Bitwise Behavior in GPU Kernels with Tensor Core: Black-Box
+  Reconstruction, Compiler Enforcement, and Static Verification", arXiv
+  2609.11356, Abstract.  Reduction order is the main source of bit-level
+  differences, next to partial-sum precision, fused multiply-add and where
+  rounding happens; a balanced-tree order can be enforced to make results
+  reproducible.
+
+What it computes:
+
+* ``exact_sum`` / ``exact_row_sums`` -- the plain definition of the result: the
+  exact real sum of the binary16 inputs, held as an integer count of 2^-24,
+  rounded once (round-to-nearest-even) to binary32 or binary64.
+* ``fixed_tree_sum`` / ``fixed_tree_row_sums`` -- the prescribed fixed order:
+  a balanced binary tree over the inputs (padded to a power of two with -0.0),
+  every node one binary32 round-to-nearest-even addition.
+
+Every function is pinned by tests under ``tests/`` to something other than
+itself (library routines, brute force with rationals, closed forms, worked
+examples and invariants); none is "parity unpinned".
+"""
+from .binary16 import decode_table, decode_bits, BINARY16_QUANTUM_EXP
+from .rounding import round_scaled_int, to_binary32, to_binary64
+from .exact import ExactSum, exact_sum, exact_row_sums
+from .tree import fixed_tree_sum, fixed_tree_row_sums
+
+__all__ = [
+    "decode_table", "decode_bits", "BINARY16_QUANTUM_EXP",
+    "round_scaled_int", "to_binary32", "to_binary64",
+    "ExactSum", "exact_sum", "exact_row_sums",
+    "fixed_tree_sum", "fixed_tree_row_sums",
+]
