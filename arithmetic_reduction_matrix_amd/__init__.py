@@ -1,0 +1,202 @@
+"""fp16 sum-reduction on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libarmx.so`` (declared in
+``include/armx.h``): it checks tensor types, allocates output and workspace
+with PyTorch on the input's device, passes raw device pointers and the
+current HIP stream, and turns status codes into exceptions.  Every step of
+the reduction runs in the library's HIP kernels; there is no fallback.
+
+Entry points (same names as the C ABI):
+
+* ``reduce_sum(x)`` -- sum of a float16 tensor as a 0-dim float32 tensor, by
+  chained MFMAs against an all-ones operand ("GPU Tensor Cores for fast
+  Arithmetic Reductions", arXiv 2001.05585, Abstract); ``plain=True`` selects
+  the MFMA-free comparison design.
+* ``reduce_rows(x)`` -- float32 sum of every row of a 2-D float16 tensor.
+* ``reduce_sum_fixed_order(x)`` -- sum in one prescribed balanced-tree order,
+  bit-identical for every configuration ("Taming Bitwise Behavior in GPU
+  Kernels with Tensor Core", arXiv 2609.11356, Abstract).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "workspace_bytes",
+    "ArmxError", "Config", "LIB_PATH", "OP_SUM", "OP_ROWS", "OP_FIXED",
+    "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so")
+
+OP_SUM, OP_ROWS, OP_FIXED = 0, 1, 2
+FLAG_PLAIN, FLAG_CACHED_LOADS, FLAG_ONE_CHAIN, FLAG_TWO_PASS = 0x1, 0x2, 0x4, 0x8
+
+_STATUS = {
+    0: "ARMX_OK", -1: "ARMX_ERR_NULL", -2: "ARMX_ERR_ALIGN", -3: "ARMX_ERR_CONFIG",
+    -4: "ARMX_ERR_WORKSPACE", -5: "ARMX_ERR_SHAPE", -6: "ARMX_ERR_HIP",
+}
+
+
+class ArmxError(RuntimeError):
+    """A call into libarmx returned a negative status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = _STATUS.get(status, "unknown")
+
+
+class Config(ctypes.Structure):
+    """Mirror of ``armx_config``."""
+
+    _fields_ = [("block_threads", ctypes.c_int), ("chain_r", ctypes.c_int),
+                ("grid_blocks", ctypes.c_int), ("flags", ctypes.c_uint)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m arithmetic_reduction_matrix_amd._build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, cfgp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Config)
+    lib.reduce_sum.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
+    lib.reduce_sum_fixed_order.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
+    lib.reduce_rows.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
+    for f in (lib.reduce_sum, lib.reduce_sum_fixed_order, lib.reduce_rows):
+        f.restype = ctypes.c_int
+    lib.armx_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, cfgp]
+    lib.armx_workspace_bytes.restype = sz
+    lib.armx_status_string.argtypes = [ctypes.c_int]
+    lib.armx_status_string.restype = ctypes.c_char_p
+    lib.armx_version.argtypes = []
+    lib.armx_version.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _config(block_threads=0, chain_r=0, grid_blocks=0, plain=False, cached_loads=False,
+            one_chain=False, two_pass=False) -> Config:
+    flags = ((FLAG_PLAIN if plain else 0) | (FLAG_CACHED_LOADS if cached_loads else 0)
+             | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0))
+    return Config(int(block_threads), int(chain_r), int(grid_blocks), flags)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = lib.armx_status_string(status).decode()
+        raise ArmxError(status, f"{what}: {msg}")
+
+
+def workspace_bytes(op: int, n_or_rows: int, cols: int = 0, **cfg) -> int:
+    """Bytes of workspace the matching call needs (0 if none)."""
+    c = _config(**cfg)
+    v = lib.armx_workspace_bytes(int(op), int(n_or_rows), int(cols), ctypes.byref(c))
+    if v == ctypes.c_size_t(-1).value:
+        raise ArmxError(-3, "armx_workspace_bytes: invalid op or configuration")
+    return int(v)
+
+
+# Zero-filled workspaces, one per (device, stream); a call leaves its
+# workspace's counter at zero, so calls on one stream can share one.
+_ws_lock = threading.Lock()
+_ws_cache: dict[tuple[int, int], torch.Tensor] = {}
+
+
+def _workspace(device: torch.device, stream: int, nbytes: int) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    key = (device.index, stream)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            size = max(nbytes, 1 << 16)
+            ws = torch.zeros(size, dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def _check_input(x: torch.Tensor, ndim: int | None, name: str) -> None:
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if x.dtype != torch.float16:
+        raise TypeError(f"{name}: expected float16, got {x.dtype}")
+    if not x.is_cuda:
+        raise ValueError(f"{name}: the input must be on a GPU (HIP) device")
+    if ndim is not None and x.dim() != ndim:
+        raise ValueError(f"{name}: expected a {ndim}-D tensor, got {x.dim()}-D")
+
+
+def _flat_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config, name: str):
+    _check_input(x, None, name)
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: the input must be contiguous")
+    n = x.numel()
+    dev = x.device
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        if out is None:
+            out = torch.empty((), dtype=torch.float32, device=dev)
+        elif out.dtype != torch.float32 or out.device != dev or out.numel() < 1:
+            raise ValueError(f"{name}: out must be a float32 tensor on {dev}")
+        need = lib.armx_workspace_bytes(op, n, 0, ctypes.byref(cfg))
+        if need == ctypes.c_size_t(-1).value:
+            _check(-3, name)
+        if workspace is None:
+            ws = _workspace(dev, stream, need)
+        else:
+            ws = workspace
+        ws_ptr = ws.data_ptr() if ws is not None else None
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+        st = fn(x.data_ptr() if n else None, n, out.data_ptr(), ws_ptr, ws_bytes,
+                ctypes.byref(cfg), stream)
+    _check(st, name)
+    return out
+
+
+def reduce_sum(x: torch.Tensor, *, out: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+    """Sum of all elements of a contiguous float16 GPU tensor, as float32.
+
+    Keyword configuration: block_threads, chain_r, grid_blocks, plain,
+    cached_loads, one_chain, two_pass (see ``include/armx.h``).  A workspace
+    passed explicitly must be zero-filled before its first use.
+    """
+    return _flat_call(lib.reduce_sum, OP_SUM, x, out, workspace, _config(**cfg), "reduce_sum")
+
+
+def reduce_sum_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
+                           workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+    """Balanced-tree-order sum of a contiguous float16 GPU tensor, as float32;
+    the same bits for every configuration."""
+    return _flat_call(lib.reduce_sum_fixed_order, OP_FIXED, x, out, workspace, _config(**cfg),
+                      "reduce_sum_fixed_order")
+
+
+def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+    """float32 sum of every row of a 2-D float16 GPU tensor whose rows are
+    contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8."""
+    _check_input(x, 2, "reduce_rows")
+    rows, cols = x.shape
+    if cols > 1 and x.stride(1) != 1:
+        raise ValueError("reduce_rows: rows must be contiguous (stride(1) == 1)")
+    ld = x.stride(0) if rows > 1 and cols > 0 else cols
+    dev = x.device
+    c = _config(**cfg)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        if out is None:
+            out = torch.empty(rows, dtype=torch.float32, device=dev)
+        elif out.dtype != torch.float32 or out.device != dev or out.numel() < rows:
+            raise ValueError(f"reduce_rows: out must be a float32 tensor of {rows} on {dev}")
+        st = lib.reduce_rows(x.data_ptr() if x.numel() else None, rows, cols, ld,
+                             out.data_ptr() if rows else None, None, 0, ctypes.byref(c), stream)
+    _check(st, "reduce_rows")
+    return out

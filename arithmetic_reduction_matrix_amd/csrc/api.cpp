@@ -1,0 +1,114 @@
+// The C entry points declared in include/armx.h: check arguments, make a
+// plan, enqueue kernels on the caller's stream.  Nothing here allocates.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+
+#include "armx.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device (cached); 256 if no device is usable.
+int current_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return 256;
+  g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_ws(const armx::Plan& plan, const void* ws, size_t ws_bytes) {
+  if (plan.ws_bytes == 0) return ARMX_OK;
+  if (!ws) return ARMX_ERR_NULL;
+  if (!aligned(ws, 256)) return ARMX_ERR_ALIGN;
+  if (ws_bytes < plan.ws_bytes) return ARMX_ERR_WORKSPACE;
+  return ARMX_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ARMX_OK : ARMX_ERR_HIP; }
+
+// Common checks of reduce_sum and reduce_sum_fixed_order.
+int prepare_flat(int op, const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
+                 const armx_config* cfg, armx::Plan* plan) {
+  if (!out) return ARMX_ERR_NULL;
+  if (n > 0 && !x) return ARMX_ERR_NULL;
+  if (n > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  // configuration errors are reported before touching the device
+  armx::Plan probe;
+  int st = armx::make_plan(op, n, 0, 0, cfg, 256, &probe);
+  if (st != ARMX_OK) return st;
+  st = armx::make_plan(op, n, 0, 0, cfg, n > 0 ? current_cu_count() : 256, plan);
+  if (st != ARMX_OK) return st;
+  return check_ws(*plan, ws, ws_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
+               const armx_config* cfg, void* stream) {
+  armx::Plan plan;
+  int st = prepare_flat(armx::kOpSum, x, n, out, ws, ws_bytes, cfg, &plan);
+  if (st != ARMX_OK) return st;
+  return hip_status(armx::launch_sum(plan, x, out, ws, static_cast<hipStream_t>(stream)));
+}
+
+int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
+                           const armx_config* cfg, void* stream) {
+  armx::Plan plan;
+  int st = prepare_flat(armx::kOpFixed, x, n, out, ws, ws_bytes, cfg, &plan);
+  if (st != ARMX_OK) return st;
+  return hip_status(armx::launch_fixed(plan, x, out, ws, static_cast<hipStream_t>(stream)));
+}
+
+int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, void* ws,
+                size_t ws_bytes, const armx_config* cfg, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (rows > 0 && !out) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  armx::Plan plan;
+  int st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg, 256, &plan);
+  if (st != ARMX_OK) return st;
+  return hip_status(armx::launch_rows(plan, x, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_config* cfg) {
+  armx::Plan plan;
+  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED) return size_t(-1);
+  const int cus = (op == ARMX_OP_ROWS || n_or_rows == 0) ? 256 : current_cu_count();
+  if (armx::make_plan(op, n_or_rows, cols, cols, cfg, cus, &plan) != ARMX_OK) return size_t(-1);
+  return plan.ws_bytes;
+}
+
+const char* armx_status_string(int status) {
+  switch (status) {
+    case ARMX_OK: return "ARMX_OK";
+    case ARMX_ERR_NULL: return "ARMX_ERR_NULL: a required pointer is NULL";
+    case ARMX_ERR_ALIGN: return "ARMX_ERR_ALIGN: misaligned pointer or row pitch";
+    case ARMX_ERR_CONFIG: return "ARMX_ERR_CONFIG: invalid block size, chain length, grid or flags";
+    case ARMX_ERR_WORKSPACE: return "ARMX_ERR_WORKSPACE: workspace too small";
+    case ARMX_ERR_SHAPE: return "ARMX_ERR_SHAPE: invalid or too large sizes";
+    case ARMX_ERR_HIP: return "ARMX_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown armx status";
+  }
+}
+
+int armx_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+// Device helpers for the gfx950 reduction kernels.
+//
+// Data layout used by every kernel: the input is a contiguous array of
+// binary16 values.  One wavefront load is 64 lanes x 16 bytes: lane l reads
+// the 8 consecutive values [8l, 8l + 8) of a 512-value "chunk", so a load is
+// fully coalesced (1 KiB contiguous) and is exactly one 32 x 16 B operand of
+// v_mfma_f32_16x16x32_f16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace armx {
+namespace dev {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLanes = 64;
+
+__device__ __forceinline__ int lane_id() { return int(threadIdx.x) & 63; }
+// wave-uniform by construction; readfirstlane lets the compiler keep it (and
+// everything derived from it) in scalar registers
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+}
+__device__ __forceinline__ int num_waves() { return int(blockDim.x) >> 6; }
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if constexpr (NT) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+// 8 binary16 values starting at element e of xh; elements at or beyond n are
+// replaced by `fill` (a binary16 bit pattern).  Only used for the one chunk
+// that straddles the end of the input, so scalar loads are fine here.
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* __restrict__ xh, uint64_t e,
+                                              uint64_t n, uint32_t fill) {
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (e + i < n) ? uint32_t(xh[e + i]) : fill;
+  u32x4 v;
+  v[0] = h[0] | (h[1] << 16);
+  v[1] = h[2] | (h[3] << 16);
+  v[2] = h[4] | (h[5] << 16);
+  v[3] = h[6] | (h[7] << 16);
+  return v;
+}
+
+// ---- cross-lane moves -------------------------------------------------------
+
+__device__ __forceinline__ int fbits(float v) { return __builtin_bit_cast(int, v); }
+__device__ __forceinline__ float bitsf(int v) { return __builtin_bit_cast(float, v); }
+
+// DPP controls (GCN/CDNA encoding)
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of each 8 reads lane 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of each 16 reads lane 15 - i
+constexpr int kDppRor8 = 0x128;       // row_ror:8
+constexpr int kDppRor4 = 0x124;
+constexpr int kDppRor2 = 0x122;
+constexpr int kDppRor1 = 0x121;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return bitsf(__builtin_amdgcn_update_dpp(0, fbits(v), CTRL, 0xF, 0xF, false));
+}
+
+// v + (v of lane l ^ 16): v_permlane16_swap exchanges the odd 16-lane rows of
+// its first operand with the even rows of its second; with both operands v,
+// the two results hold rows (0,0,2,2) and (1,1,3,3), so their sum pairs every
+// lane with lane ^ 16.
+__device__ __forceinline__ float add_xor16(float v) {
+  auto p = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  return bitsf(int(p[0])) + bitsf(int(p[1]));
+}
+
+// v + (v of lane l ^ 32), by the same argument with v_permlane32_swap.
+__device__ __forceinline__ float add_xor32(float v) {
+  auto p = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  return bitsf(int(p[0])) + bitsf(int(p[1]));
+}
+
+// ---- fixed pairing ladder ---------------------------------------------------
+//
+// Level j (1-based) adds the values of aligned lane groups of size 2^(j-1)
+// pairwise, provided every lane of a group already holds that group's value:
+//   level 1: lane ^ 1, level 2: lane ^ 2 (quad permutes),
+//   level 3: mirror within 8 lanes (reaches the other group of 4),
+//   level 4: mirror within 16 lanes (reaches the other group of 8),
+//   level 5: lane ^ 16, level 6: lane ^ 32.
+// Both partners compute a + b or b + a, which are the same binary32 value, so
+// after level j every lane of a group of 2^j holds the same node of a
+// balanced binary tree over the lanes.  `levels` must be wave-uniform.
+__device__ __forceinline__ float lane_tree(float v, int levels) {
+  if (levels >= 1) v = v + dpp<kDppXor1>(v);
+  if (levels >= 2) v = v + dpp<kDppXor2>(v);
+  if (levels >= 3) v = v + dpp<kDppHalfMirror>(v);
+  if (levels >= 4) v = v + dpp<kDppMirror>(v);
+  if (levels >= 5) v = add_xor16(v);
+  if (levels >= 6) v = add_xor32(v);
+  return v;
+}
+
+__device__ __forceinline__ float lane_tree_full(float v) {
+  v = v + dpp<kDppXor1>(v);
+  v = v + dpp<kDppXor2>(v);
+  v = v + dpp<kDppHalfMirror>(v);
+  v = v + dpp<kDppMirror>(v);
+  v = add_xor16(v);
+  return add_xor32(v);
+}
+
+// Sum of the 16 lanes of each 16-lane row, in every lane of the row (the
+// order differs between lanes; callers read one fixed lane).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<kDppRor8>(v);
+  v += dpp<kDppRor4>(v);
+  v += dpp<kDppRor2>(v);
+  v += dpp<kDppRor1>(v);
+  return v;
+}
+
+// Sum over all 64 lanes (every lane gets the same value).
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v = add_xor16(v);
+  return add_xor32(v);
+}
+
+// ---- binary16 -> binary32 ---------------------------------------------------
+
+__device__ __forceinline__ float lo_f32(uint32_t w) {
+  return float(__builtin_bit_cast(half2v, w)[0]);
+}
+__device__ __forceinline__ float hi_f32(uint32_t w) {
+  return float(__builtin_bit_cast(half2v, w)[1]);
+}
+
+// ---- the MFMA tile step -------------------------------------------------------
+//
+// acc += ONES(16x32) * T(32x16), with T the 512 values of one wavefront load.
+// Lane l supplies column l % 16 of T, so acc (in every lane l) becomes the
+// running sum of column l % 16, i.e. of the values loaded by the lanes
+// congruent to l mod 16.  Products by 1.0 are exact; accumulation is fp32.
+__device__ __forceinline__ floatx4 mfma_ones(floatx4 acc, u32x4 tile) {
+  const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, __builtin_bit_cast(half8, tile), acc, 0,
+                                                0, 0);
+}
+
+// Sum of one 16-byte load's 8 values, converted and added in fp32 (the
+// MFMA-free design).
+__device__ __forceinline__ void plain_add8(float& a, float& b, u32x4 t) {
+  a += lo_f32(t[0]);
+  b += hi_f32(t[0]);
+  a += lo_f32(t[1]);
+  b += hi_f32(t[1]);
+  a += lo_f32(t[2]);
+  b += hi_f32(t[2]);
+  a += lo_f32(t[3]);
+  b += hi_f32(t[3]);
+}
+
+// ---- streaming chains of tiles ----------------------------------------------
+
+// Loads chain c of R chunks: R x 16 bytes per lane from base + c * R chunks.
+template <int R, bool NT>
+__device__ __forceinline__ void load_chain(const u32x4* __restrict__ base, uint64_t c, int lane,
+                                           u32x4 (&v)[R]) {
+  const u32x4* p = base + c * (uint64_t(R) * 64) + lane;
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = load16<NT>(p + r * 64);
+}
+
+// One chain: R tile steps whose fp32 result starts from zero and is then
+// added (one round-to-nearest-even v_add_f32) into the running per-lane sum
+// `run`.  Keeping each chain's sub-result separate is what holds the error
+// down: a single accumulator carried across many MFMAs grows large, and the
+// MFMA's own accumulation then loses low bits on every step.
+//   MFMA design: lane l's chain result is the sum of column l % 16 of the R
+//   tiles (the same value in all four accumulator registers).
+//   MFMA-free design: lane l's chain result is the sum of its own 8 R values.
+template <int R, bool PLAIN>
+__device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
+  if constexpr (PLAIN) {
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) plain_add8(a, b, v[r]);
+    run += a + b;
+  } else {
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc = mfma_ones(acc, v[r]);
+    run += acc[0];
+  }
+}
+
+// Accumulates the full chains c0, c0 + stride, ..., (`iters` of them).
+// Software pipeline, unrolled by two with ping-pong buffers: the next chain's
+// R loads are issued before the current chain's R tile steps, so a wavefront
+// keeps up to 2R loads in flight and no registers are copied.  Every load in
+// the loop is unconditional -- a branch around a load makes the compiler wait
+// for all loads where the paths join -- so a prefetch past the last chain
+// re-reads that chain (still in L2) and its values are not used.
+template <int R, bool NT, bool PLAIN>
+__device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, uint64_t c0,
+                                              uint64_t iters, uint64_t stride, int lane,
+                                              float& run) {
+  if (iters == 0) return;
+  const uint64_t last = c0 + (iters - 1) * stride;
+  u32x4 a[R], b[R];
+  load_chain<R, NT>(base, c0, lane, a);
+  for (uint64_t j = 0; j < iters; j += 2) {
+    load_chain<R, NT>(base, j + 1 < iters ? c0 + (j + 1) * stride : last, lane, b);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
+    chain_step<R, PLAIN>(a, run);
+    load_chain<R, NT>(base, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, a);
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < iters) chain_step<R, PLAIN>(b, run);
+  }
+}
+
+// The partial chain c (elements [c R 512, end) of a segment of `len` values
+// starting at xh); values past `len` count as +0.0.
+template <int R, bool PLAIN>
+__device__ __forceinline__ void tail_chain(const uint16_t* __restrict__ xh, uint64_t c,
+                                           uint64_t len, int lane, float& run) {
+  u32x4 v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint64_t e = (c * R + r) * 512 + uint64_t(lane) * 8;
+    v[r] = e < len ? load8_masked(xh, e, len, 0u) : u32x4{0u, 0u, 0u, 0u};
+  }
+  chain_step<R, PLAIN>(v, run);
+}
+
+// The wavefront total of the running per-lane sums (valid in every lane).
+template <bool PLAIN>
+__device__ __forceinline__ float wave_total(float run) {
+  if constexpr (PLAIN) {
+    return wave_sum(run);
+  } else {
+    // lanes 0..15 hold the 16 column totals (lanes 16..63 repeat them)
+    return row16_sum(run);
+  }
+}
+
+// ---- block combine and completion ticket ------------------------------------
+
+// Sum of one value per wavefront (taken from lane 0) over the block; the result
+// is valid in thread 0.  `red` is LDS of at least 16 floats.
+__device__ __forceinline__ float block_sum_lane0(float t, float* red) {
+  __syncthreads();  // red may still be read by a previous call
+  if (lane_id() == 0) red[wave_id()] = t;
+  __syncthreads();
+  float v = 0.0f;
+  if (wave_id() == 0) {
+    v = lane_id() < num_waves() ? red[lane_id()] : 0.0f;
+    v = row16_sum(v);
+  }
+  return v;
+}
+
+// Completion ticket.  Thread 0 publishes this block's result in `slot` with
+// an agent-scope atomic store (written through to the level that all XCDs
+// share), waits until that store is complete (s_waitcnt vmcnt(0)), then
+// increments `counter`.  The block whose increment is the last one sees every
+// other block's result through agent-scope atomic loads (load_published).
+// No agent-scope release fence is used: on gfx950 that fence writes back the
+// whole L2 of the XCD, and one per block costs more than the reduction itself.
+// The last block returns the counter to zero for the next call on the same
+// workspace.  Called by every thread; returns true in the last block only.
+__device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
+                                                       unsigned* counter, int* flag) {
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(slot, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const unsigned prev =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == gridDim.x - 1;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// A block result written by publish_and_check_last (or by an earlier kernel).
+__device__ __forceinline__ float load_published(const float* slot) {
+  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace dev
+}  // namespace armx

@@ -1,0 +1,120 @@
+// Argument checking and launch planning (host only, no HIP calls).
+#include "plan.h"
+
+namespace armx {
+namespace {
+
+constexpr unsigned kKnownFlags = ARMX_FLAG_PLAIN | ARMX_FLAG_CACHED_LOADS |
+                                 ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS;
+
+uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(uint64_t v) { return v && !(v & (v - 1)); }
+
+int log2_ceil(uint64_t v) {
+  int k = 0;
+  while ((uint64_t(1) << k) < v) ++k;
+  return k;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
+              const armx_config* cfg, int cu_count, Plan* plan) {
+  const OpDefaults d = op == kOpFixed ? kFixedDefaults : op == kOpRows ? kRowsDefaults
+                                                                      : kSumDefaults;
+  armx_config c{};
+  if (cfg) c = *cfg;
+  if (c.block_threads == 0) c.block_threads = d.block;
+  if (c.chain_r == 0) c.chain_r = d.r;
+  if (c.block_threads < 64 || c.block_threads > 64 * kMaxWaves || c.block_threads % 64)
+    return ARMX_ERR_CONFIG;
+  if (c.chain_r < 1 || c.chain_r > kMaxR) return ARMX_ERR_CONFIG;
+  if (c.grid_blocks < 0) return ARMX_ERR_CONFIG;
+  if (c.flags & ~kKnownFlags) return ARMX_ERR_CONFIG;
+  if (cu_count <= 0) cu_count = 256;
+
+  Plan p;
+  p.op = op;
+  p.waves = c.block_threads / 64;
+  p.r = c.chain_r;
+  p.flags = c.flags;
+  const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
+
+  if (op == kOpSum) {
+    const uint64_t n = n_or_rows;
+    if (n > kMaxN) return ARMX_ERR_SHAPE;
+    p.n = n;
+    if (n == 0) { *plan = p; return ARMX_OK; }
+    const uint64_t chains = ceil_div(n, kChunk * R);
+    uint64_t grid = ceil_div(chains, W);
+    if (!(c.flags & ARMX_FLAG_ONE_CHAIN)) {
+      uint64_t resident = uint64_t(cu_count) * uint64_t(d.waves_per_cu) / W;
+      if (resident < 1) resident = 1;
+      if (grid > resident) grid = resident;
+    }
+    if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) {
+      if (c.flags & ARMX_FLAG_ONE_CHAIN) return ARMX_ERR_CONFIG;  // would not be one chain
+      grid = uint64_t(c.grid_blocks);
+    }
+    if (grid < 1) grid = 1;
+    if (grid > 0x7FFFFFFFull) return ARMX_ERR_SHAPE;
+    p.grid = int(grid);
+    p.ws_bytes = kCounterBytes + round_up(sizeof(float) * size_t(grid), 256);
+  } else if (op == kOpFixed) {
+    const uint64_t n = n_or_rows;
+    if (n > kMaxN) return ARMX_ERR_SHAPE;
+    if (!is_pow2(W)) return ARMX_ERR_CONFIG;
+    if (c.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_ONE_CHAIN)) return ARMX_ERR_CONFIG;
+    p.n = n;
+    if (n == 0) { *plan = p; return ARMX_OK; }
+    const uint64_t chunks = ceil_div(n, kChunk);
+    uint64_t target = uint64_t(cu_count) * uint64_t(d.waves_per_cu) / W;
+    if (c.grid_blocks > 0 && target > uint64_t(c.grid_blocks)) target = uint64_t(c.grid_blocks);
+    if (target > uint64_t(kFixedMaxBlocks)) target = kFixedMaxBlocks;
+    if (target < 1) target = 1;
+    // every wavefront owns an aligned power-of-two range of chunks, so every
+    // wavefront and every block covers a complete subtree of the tree
+    int lc = log2_ceil(ceil_div(chunks, W * target));
+    if (lc > kFixedMaxLog2Chunks) return ARMX_ERR_SHAPE;
+    p.log2_chunks = lc;
+    const uint64_t grid = ceil_div(chunks, W << lc);
+    if (grid > uint64_t(kFixedMaxBlocks)) return ARMX_ERR_SHAPE;
+    p.grid = int(grid);
+    p.ws_bytes = kCounterBytes + round_up(sizeof(float) * size_t(grid), 256);
+  } else if (op == kOpRows) {
+    if (c.flags & (ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS)) return ARMX_ERR_CONFIG;
+    const uint64_t rows = n_or_rows;
+    if (ld < cols) return ARMX_ERR_SHAPE;
+    if (cols > kMaxN || rows > kMaxN || (rows > 0 && ld > kMaxN / rows)) return ARMX_ERR_SHAPE;
+    if (rows > 1 && cols > 0 && ld % 8) return ARMX_ERR_ALIGN;
+    p.rows = rows;
+    p.n = cols;
+    p.ld = ld;
+    // many rows: one wavefront per row over a persistent grid; few rows: a
+    // block per row so that every row still gets W wavefronts
+    uint64_t waves = uint64_t(cu_count) * uint64_t(d.waves_per_cu);
+    uint64_t grid;
+    if (rows >= waves) {
+      p.mode = 1;
+      grid = ceil_div(waves, W);
+      if (grid > ceil_div(rows, W)) grid = ceil_div(rows, W);
+    } else {
+      p.mode = 0;
+      grid = rows;
+    }
+    if (grid > (uint64_t(1) << 20)) grid = uint64_t(1) << 20;   // blocks loop over rows
+    if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) grid = uint64_t(c.grid_blocks);
+    if (grid < 1) grid = 1;
+    p.grid = int(grid);
+    p.ws_bytes = 0;
+  } else {
+    return ARMX_ERR_CONFIG;
+  }
+  *plan = p;
+  return ARMX_OK;
+}
+
+}  // namespace armx

@@ -1,0 +1,60 @@
+// Launch planning shared by the C entry points and the kernel launchers.
+// Plain C++: no HIP types, so argument checking and grid sizing can be
+// exercised without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "armx.h"
+
+namespace armx {
+
+// One wavefront load: 64 lanes x 16 bytes = 512 binary16 values.  It is also
+// one B operand of v_mfma_f32_16x16x32_f16 (32 x 16 values).
+constexpr uint64_t kChunk = 512;
+// Leaf tile of the fixed-order tree (a complete depth-8 subtree).
+constexpr uint64_t kTile = 256;
+constexpr int kMaxR = 8;
+constexpr int kMaxWaves = 16;
+// Per-operation defaults (block threads, chain length R) and the number of
+// wavefronts per compute unit an automatic persistent grid aims at.
+struct OpDefaults {
+  int block;
+  int r;
+  int waves_per_cu;
+};
+constexpr OpDefaults kSumDefaults{128, 8, 2};
+constexpr OpDefaults kFixedDefaults{256, 8, 4};
+constexpr OpDefaults kRowsDefaults{64, 8, 2};
+// The fixed-order final combine handles at most this many block results.
+constexpr int kFixedMaxBlocks = 4096;
+// Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.
+constexpr int kFixedMaxLog2Chunks = 24;
+// Workspace: the completion counter sits in the first kCounterBytes.
+constexpr size_t kCounterBytes = 256;
+constexpr uint64_t kMaxN = uint64_t(1) << 40;
+
+enum Op { kOpSum = ARMX_OP_SUM, kOpRows = ARMX_OP_ROWS, kOpFixed = ARMX_OP_FIXED };
+
+struct Plan {
+  int op = 0;
+  int waves = 0;            // wavefronts per block (W)
+  int r = 0;                // loads per wavefront per step (R)
+  int grid = 0;             // blocks launched
+  unsigned flags = 0;
+  int log2_chunks = 0;      // fixed order: 2^log2_chunks chunks per wavefront
+  int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row
+  uint64_t n = 0;           // elements (sum / fixed); columns (rows)
+  uint64_t rows = 0;
+  uint64_t ld = 0;
+  size_t ws_bytes = 0;      // workspace the launch needs
+};
+
+// Resolves and checks a configuration for `op`.  `cu_count` is the number of
+// compute units of the target device.  Returns ARMX_OK or a negative status;
+// pointers are not examined here.
+int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
+              const armx_config* cfg, int cu_count, Plan* plan);
+
+}  // namespace armx

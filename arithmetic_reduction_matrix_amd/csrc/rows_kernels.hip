@@ -1,0 +1,164 @@
+// Row-segmented sum: out[r] = sum of x[r * ld + c] over c < cols.
+//
+// Many independent sums of the kind in "GPU Tensor Cores for fast Arithmetic
+// Reductions" (arXiv 2001.05585), Abstract, one per row.  Every chunk of a
+// row goes through one v_mfma_f32_16x16x32_f16 against all-ones (or, with
+// ARMX_FLAG_PLAIN, per-lane fp32 adds) and R of them chain into the fp32
+// accumulators.  A chunk never straddles two rows: the chunk grid restarts
+// at every row (rows are 16-byte aligned because ld is a multiple of 8), and
+// a row's last partial chain is masked.  The row's fp32 total is written
+// directly -- no workspace, no second pass.  Two mappings:
+//  * wave_rows: each wavefront sums whole rows (rows g, g + T, ... for
+//    wavefront g of T); when rows are whole numbers of chains the loads of
+//    the next row are issued before the current row is finished, so the
+//    pipeline runs across rows; no block synchronisation at all.  Used when
+//    there are many rows.
+//  * otherwise each block sums a row (looping over rows if needed) and its W
+//    wavefronts take the row's chains round-robin, combined through LDS.
+#include "device_common.hpp"
+#include "launch.h"
+
+namespace armx {
+namespace {
+
+using namespace dev;
+
+// Position in this wavefront's sequence of (row, chain) items: rows
+// g, g + T, g + 2T, ... (k counts them) and chains 0 .. cpr-1 of each.
+struct RowCursor {
+  uint64_t k = 0, c = 0;
+};
+
+// The flattened stream of one wavefront's rows when every row is a whole
+// number of chains: loads run ahead across row boundaries, so the pipeline
+// never drains between rows.  At the end of a row its total is written and
+// the running sum restarts.
+template <int R, bool NT, bool PLAIN>
+__device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64_t rows,
+                                          uint64_t cpr, uint64_t ld, float* __restrict__ out,
+                                          uint64_t g, uint64_t T, int lane) {
+  if (g >= rows) return;
+  const uint64_t K = (rows - 1 - g) / T + 1;
+  const uint64_t items = K * cpr;
+  RowCursor pf, pr;   // next item to load, next item to reduce
+  auto ptr = [&](const RowCursor& q) {
+    return reinterpret_cast<const u32x4*>(x + (g + q.k * T) * ld) + q.c * (uint64_t(R) * 64);
+  };
+  auto advance_load = [&]() {
+    // stays on the last item once it is reached (the re-read is not used)
+    if (pf.c + 1 < cpr) {
+      ++pf.c;
+    } else if (pf.k + 1 < K) {
+      pf.c = 0;
+      ++pf.k;
+    }
+  };
+  float run = 0.0f;
+  auto reduce = [&](const u32x4 (&v)[R]) {
+    chain_step<R, PLAIN>(v, run);
+    if (++pr.c == cpr) {
+      const float total = wave_total<PLAIN>(run);
+      if (lane == 0) out[g + pr.k * T] = total;
+      run = 0.0f;
+      pr.c = 0;
+      ++pr.k;
+    }
+  };
+  u32x4 a[R], b[R];
+  load_chain<R, NT>(ptr(pf), 0, lane, a);
+  advance_load();
+  for (uint64_t j = 0; j < items; j += 2) {
+    load_chain<R, NT>(ptr(pf), 0, lane, b);
+    advance_load();
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
+    reduce(a);
+    load_chain<R, NT>(ptr(pf), 0, lane, a);
+    advance_load();
+    __builtin_amdgcn_sched_barrier(0);
+    if (j + 1 < items) reduce(b);
+  }
+}
+
+template <int R, bool NT, bool PLAIN>
+__global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__ x, uint64_t rows,
+                                                    uint64_t cols, uint64_t ld,
+                                                    float* __restrict__ out, int wave_rows) {
+  __shared__ float red[16];
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t chains_full = cols / (uint64_t(R) * 512);
+  const bool tail = chains_full * R * 512 < cols;
+
+  if (wave_rows) {
+    const uint64_t total_waves = uint64_t(gridDim.x) * W;
+    const uint64_t g = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
+    if (!tail) {
+      rows_flat<R, NT, PLAIN>(x, rows, chains_full, ld, out, g, total_waves, lane);
+      return;
+    }
+    for (uint64_t row = g; row < rows; row += total_waves) {
+      const uint16_t* xr = x + row * ld;
+      float run = 0.0f;
+      stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane,
+                                  run);
+      tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
+      const float total = wave_total<PLAIN>(run);
+      if (lane == 0) out[row] = total;
+    }
+    return;
+  }
+
+  for (uint64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const uint16_t* xr = x + row * ld;
+    float run = 0.0f;
+    const uint64_t c = uint64_t(wave_id());
+    const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / W + 1 : 0;
+    stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), c, iters, W, lane, run);
+    if (tail && c + iters * W == chains_full) tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
+    const float total = block_sum_lane0(wave_total<PLAIN>(run), red);
+    if (threadIdx.x == 0) out[row] = total;
+  }
+}
+
+template <int R, bool NT, bool PLAIN>
+const void* rows_ptr() {
+  return reinterpret_cast<const void*>(&rows_kernel<R, NT, PLAIN>);
+}
+
+template <int R>
+const void* pick_rows(bool nt, bool plain) {
+  if (nt) return plain ? rows_ptr<R, true, true>() : rows_ptr<R, true, false>();
+  return plain ? rows_ptr<R, false, true>() : rows_ptr<R, false, false>();
+}
+
+const void* rows_kernel_for(int r, bool nt, bool plain) {
+  switch (r) {
+    case 1: return pick_rows<1>(nt, plain);
+    case 2: return pick_rows<2>(nt, plain);
+    case 3: return pick_rows<3>(nt, plain);
+    case 4: return pick_rows<4>(nt, plain);
+    case 5: return pick_rows<5>(nt, plain);
+    case 6: return pick_rows<6>(nt, plain);
+    case 7: return pick_rows<7>(nt, plain);
+    case 8: return pick_rows<8>(nt, plain);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
+  if (plan.rows == 0) return hipSuccess;
+  if (plan.n == 0) return launch_zero(out, plan.rows, stream);
+  const void* fn = rows_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                   (plan.flags & ARMX_FLAG_PLAIN) != 0);
+  if (!fn) return hipErrorInvalidValue;
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
+  int wave_rows = plan.mode;
+  void* args[] = {&xh, &rows, &cols, &ld, &out, &wave_rows};
+  return hipLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)), args, 0,
+                         stream);
+}
+
+}  // namespace armx

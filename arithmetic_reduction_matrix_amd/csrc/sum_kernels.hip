@@ -1,0 +1,150 @@
+// Free-order sum: chained MFMAs against an all-ones operand (and the MFMA-free
+// comparison design).
+//
+// "GPU Tensor Cores for fast Arithmetic Reductions" (arXiv 2001.05585),
+// Abstract: the sum of n numbers is encoded as chains of m x m
+// matrix-multiply-accumulates, each chain of R kept as a 32-bit float, and all
+// chain results are reduced into one 32-bit float.  On gfx950 one chain step
+// is v_mfma_f32_16x16x32_f16 with A = ones(16x32) and B = the 32 x 16 tile a
+// wavefront brings in with one 16-byte load per lane; R of them accumulate
+// into the same fp32 registers.  The MFMA-free design ("conventional"
+// reduction of the same Abstract) converts every value and adds it in fp32
+// per lane.
+//
+// Precision: every chain's R tile steps start from a zero fp32 accumulator,
+// and the chain result is then added into a running fp32 sum, so the MFMA
+// accumulates at most R x 32 values per column before its result is handed
+// to a round-to-nearest-even add -- the chain sub-result of the Abstract.
+//
+// Work split: a "chain" is R consecutive chunks (R x 512 values).  Wavefront
+// g of a grid of T wavefronts takes chains g, g + T, g + 2T, ...; the one
+// partial chain at the end of the input (if any) is loaded with masking by
+// the wavefront whose turn it is.  With a grid of ceil(chains / W) blocks
+// every wavefront runs exactly one chain; smaller grids loop (persistent).
+// Each block's wavefront totals are combined through LDS into one fp32 block
+// result; the last block to finish reduces the block results in index order
+// (or a second launch does, with ARMX_FLAG_TWO_PASS).  No data atomics are
+// used, so the result depends only on the configuration.
+#include "device_common.hpp"
+#include "launch.h"
+
+namespace armx {
+namespace {
+
+using namespace dev;
+
+// Reduces partials[0..count) in a fixed order with one block; valid in thread 0.
+__device__ float reduce_partials(const float* partials, unsigned count, float* red) {
+  float s = 0.0f;
+  for (unsigned i = threadIdx.x; i < count; i += blockDim.x) s += load_published(partials + i);
+  s = wave_sum(s);
+  return block_sum_lane0(s, red);
+}
+
+template <int R, bool NT, bool PLAIN>
+__global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, uint64_t n,
+                                                   uint64_t chains_full,
+                                                   float* __restrict__ partials,
+                                                   unsigned* __restrict__ counter,
+                                                   float* __restrict__ out, int two_pass) {
+  __shared__ float red[16];
+  __shared__ int flag;
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t total_waves = uint64_t(gridDim.x) * W;
+  uint64_t c = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
+
+  float run = 0.0f;
+  const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
+  stream_chains<R, NT, PLAIN>(x, c, iters, total_waves, lane, run);
+  c += iters * total_waves;
+  if (c == chains_full && chains_full * R * 512 < n) {
+    // the partial chain at the end: values past n read as +0.0
+    tail_chain<R, PLAIN>(reinterpret_cast<const uint16_t*>(x), c, n, lane, run);
+  }
+  const float block_total = block_sum_lane0(wave_total<PLAIN>(run), red);
+
+  if (gridDim.x == 1) {
+    if (threadIdx.x == 0) out[0] = block_total;
+    return;
+  }
+  if (two_pass) {
+    if (threadIdx.x == 0) partials[blockIdx.x] = block_total;
+    return;
+  }
+  if (!publish_and_check_last(partials + blockIdx.x, block_total, counter, &flag)) return;
+  const float total = reduce_partials(partials, gridDim.x, red);
+  if (threadIdx.x == 0) out[0] = total;
+}
+
+__global__ __launch_bounds__(1024) void final_sum_kernel(const float* __restrict__ partials,
+                                                         unsigned count,
+                                                         float* __restrict__ out) {
+  __shared__ float red[16];
+  const float total = reduce_partials(partials, count, red);
+  if (threadIdx.x == 0) out[0] = total;
+}
+
+__global__ void zero_kernel(float* out, uint64_t count) {
+  const uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) out[i] = 0.0f;
+}
+
+template <int R, bool NT, bool PLAIN>
+const void* sum_kernel_ptr() {
+  return reinterpret_cast<const void*>(&sum_kernel<R, NT, PLAIN>);
+}
+
+template <int R>
+const void* pick_sum(bool nt, bool plain) {
+  if (nt) return plain ? sum_kernel_ptr<R, true, true>() : sum_kernel_ptr<R, true, false>();
+  return plain ? sum_kernel_ptr<R, false, true>() : sum_kernel_ptr<R, false, false>();
+}
+
+const void* sum_kernel_for(int r, bool nt, bool plain) {
+  switch (r) {
+    case 1: return pick_sum<1>(nt, plain);
+    case 2: return pick_sum<2>(nt, plain);
+    case 3: return pick_sum<3>(nt, plain);
+    case 4: return pick_sum<4>(nt, plain);
+    case 5: return pick_sum<5>(nt, plain);
+    case 6: return pick_sum<6>(nt, plain);
+    case 7: return pick_sum<7>(nt, plain);
+    case 8: return pick_sum<8>(nt, plain);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero(float* out, uint64_t count, hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  const unsigned blocks = unsigned((count + 255) / 256);
+  void* args[] = {&out, &count};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&zero_kernel), dim3(blocks), dim3(256),
+                         args, 0, stream);
+}
+
+hipError_t launch_sum(const Plan& plan, const void* x, float* out, void* ws, hipStream_t stream) {
+  if (plan.n == 0) return launch_zero(out, 1, stream);
+  const void* fn = sum_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                  (plan.flags & ARMX_FLAG_PLAIN) != 0);
+  if (!fn) return hipErrorInvalidValue;
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  uint64_t n = plan.n;
+  uint64_t chains_full = n / (uint64_t(plan.r) * kChunk);
+  unsigned* counter = static_cast<unsigned*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  int two_pass = (plan.flags & ARMX_FLAG_TWO_PASS) ? 1 : 0;
+  void* args[] = {&xv, &n, &chains_full, &partials, &counter, &out, &two_pass};
+  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)),
+                                 args, 0, stream);
+  if (e != hipSuccess || !two_pass || plan.grid == 1) return e;
+  unsigned count = unsigned(plan.grid);
+  const float* cpart = partials;
+  void* fargs[] = {&cpart, &count, &out};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&final_sum_kernel), dim3(1), dim3(1024),
+                         fargs, 0, stream);
+}
+
+}  // namespace armx

@@ -1,0 +1,245 @@
+"""Benchmark of the fp16 sum-reduction hot path on one MI355X.
+
+One step = one reduce_sum call (chained MFMAs against ones, fp32 partials,
+block combine, completion-ticket final reduce) over n = 2^28 binary16 values
+drawn uniformly from [-1, 1) with seed 2, the input already resident in HBM.
+Two copies of the input are used in turn so that no step reads data the
+previous step left in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is elements/s over the timed steps (wall clock
+between two synchronisations); `roofline.achieved` is the algorithmic bytes of
+one launch (2 bytes per element) divided by the average launch time measured
+with HIP events recorded on the stream the kernel runs on.  `cpu_baseline` is
+the CPU oracle (exact integer sum) timed on this host.  `variants` times the
+other rows of the hot path (MFMA-free design, fixed balanced-tree order, row
+sums, one-chain-per-wavefront grids) on their own workloads.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
+                    [--no-cpu-baseline] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "elements/s and achieved HBM GB/s (% of peak), fp16 sum n=2^28"
+KERNEL_SOURCES = ["arithmetic_reduction_matrix_amd/csrc/sum_kernels.hip",
+                  "arithmetic_reduction_matrix_amd/csrc/device_common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sum_kernel_n2p28_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(n_launch_bytes: int):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    is missing or was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def event_timed(torch, fn, iters: int, warmup: int = 5):
+    """Average ms per call of fn(i), events around each call on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (s, e) in enumerate(evs):
+        s.record()
+        fn(i)
+        e.record()
+    torch.cuda.synchronize()
+    times = sorted(s.elapsed_time(e) for s, e in evs)
+    return sum(times) / len(times), times[len(times) // 2]
+
+
+def cpu_baseline(x_np, budget_s: float = 12.0):
+    """The exact-sum oracle on the host: whole passes over the input until
+    `budget_s` of CPU time is spent (at least one pass).  Returns the record
+    and the oracle's result."""
+    import oracle
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        e = oracle.exact_sum(x_np)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": passes * x_np.size / el, "unit": "elements/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of oracle.exact_sum over the n=2^28 input "
+                      f"({el:.1f} s, numpy, one thread)"}, e
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the block x R matrix (paper-faithful and persistent grids)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import arithmetic_reduction_matrix_amd as armx
+    import synth_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+
+    # ---- headline workload -------------------------------------------------
+    x_np = si.workload("sum_2p28_u11")
+    n = x_np.size
+    bufs = [torch.from_numpy(x_np).to(dev)]
+    bufs.append(bufs[0].clone())
+    out = torch.empty((), dtype=torch.float32, device=dev)
+    ws = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        armx.reduce_sum(bufs[i & 1], out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i, (s, e) in enumerate(evs):
+        s.record()
+        step(i)
+        e.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sorted(s.elapsed_time(e) for s, e in evs)
+    avg_ms = sum(launch_ms) / len(launch_ms)
+    result = float(out.item())
+
+    bytes_per_launch = 2 * n
+    achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(bytes_per_launch)
+    record = {
+        "metric": METRIC,
+        "value": n * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16->f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "sum of n=2^28 fp16 uniform[-1,1) seed 2 (512 MiB), fp32 result",
+            "n": n, "block_threads": 128, "chain_r": 8, "loads": "non-temporal",
+            "grid": "persistent, 2 wavefronts per CU", "final": "last-block ticket",
+            "input_copies_rotated": 2, "device": props.name, "cus": props.multi_processor_count,
+            "workspace_bytes": ws.numel(),
+        },
+        "hbm_gbs": bytes_per_launch * args.steps / wall / 1e9,
+        "pct_hbm_peak": 100.0 * bytes_per_launch * args.steps / wall / 1e9 / HBM_PEAK_GBS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "sum_kernel<R=8, non-temporal, MFMA>",
+            "launch_ms_avg": avg_ms, "launch_ms_median": launch_ms[len(launch_ms) // 2],
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "kernel_source_sha256_16": kernel_source_hash(),
+        },
+        "result": result,
+    }
+
+    # ---- the other rows of the hot path ---------------------------------------
+    if not args.no_variants:
+        var = {}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], plain=True), 200)
+        var["plain_shuffle_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6,
+                                     "vs_mfma": avg_ms / ms}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum(
+            bufs[i & 1], one_chain=True, block_threads=256, chain_r=4), 50)
+        var["one_chain_b256_r4_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: bufs[i & 1].sum(dtype=torch.float32), 100)
+        var["torch_sum_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
+
+        xf_np = si.workload("fixed_2p26_u11")
+        fbufs = [torch.from_numpy(xf_np).to(dev)]
+        fbufs += [fbufs[0].clone() for _ in range(3)]
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum_fixed_order(fbufs[i & 3]), 200)
+        fixed_val = armx.reduce_sum_fixed_order(fbufs[0]).cpu().numpy()
+        var["fixed_order_2p26"] = {"ms": ms, "gbs": 2 * xf_np.size / ms / 1e6,
+                                   "result_bits": int(fixed_val.view(np.uint32))}
+        del fbufs
+
+        xr_np = si.workload("rows_4096x65536_normal")
+        rbufs = [torch.from_numpy(xr_np).to(dev)]
+        rbufs.append(rbufs[0].clone())
+        rout = torch.empty(4096, dtype=torch.float32, device=dev)
+        ms, med = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout), 200)
+        var["rows_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout,
+                                                                 plain=True), 100)
+        var["rows_4096x65536_plain"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
+        del rbufs
+        record["variants"] = var
+
+    if args.sweep:
+        sweep = {}
+        for one_chain in (True, False):
+            for block in (64, 256, 1024):
+                for r in (1, 2, 4, 5):
+                    it = 20 if one_chain else 100
+                    ms, med = event_timed(torch, lambda i: armx.reduce_sum(
+                        bufs[i & 1], one_chain=one_chain, block_threads=block, chain_r=r), it)
+                    key = f"{'one_chain' if one_chain else 'persistent'}_b{block}_r{r}"
+                    sweep[key] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
+                    print(key, f"{ms * 1e3:.1f} us", f"{2 * n / ms / 1e6:.0f} GB/s",
+                          file=sys.stderr, flush=True)
+        record["sweep"] = sweep
+
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"], e = cpu_baseline(x_np)
+        record["check"] = {"exact_sum": e.f64, "abs_err": abs(result - e.f64),
+                           "rel_err": abs(result - e.f64) / abs(e.f64)}
+
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,186 @@
+/*
+ * armx.h -- fp16 sum-reduction on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation is the arithmetic reduction (sum) of n numbers, computed as
+ * chained matrix-multiply-accumulates whose other operand is all ones, with
+ * 32-bit float sub-results per chain and a 32-bit float final result:
+ *   "GPU Tensor Cores for fast Arithmetic Reductions" (arXiv 2001.05585),
+ *   Abstract.
+ * The fixed-order entry point follows the balanced-tree reduction order used
+ * to make results bitwise reproducible in
+ *   "Taming Bitwise Behavior in GPU Kernels with Tensor Core: Black-Box
+ *   Reconstruction, Compiler Enforcement, and Static Verification"
+ *   (arXiv 2609.11356), Abstract.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Inputs are IEEE binary16 ("fp16") values, little-endian, in device
+ *   memory.  Outputs are IEEE binary32 values in device memory.
+ * - All pointers except `cfg` are DEVICE pointers on the current HIP device.
+ *   `cfg` is a HOST pointer and may be NULL (all defaults).
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call only enqueues work on `stream` and returns; results are ready when
+ *   the stream reaches that point.  Nothing is copied to the host and the
+ *   host is never synchronised.
+ * - The caller owns every buffer.  The library allocates no memory and keeps
+ *   no state between calls other than a per-device cache of the compute-unit
+ *   count.
+ * - Errors are returned as a negative armx_status before anything is
+ *   enqueued; the library never prints and never aborts.  A failure reported
+ *   by the HIP runtime while enqueueing returns ARMX_ERR_HIP.
+ * - Workspace: `ws` points to at least armx_workspace_bytes(...) bytes,
+ *   256-byte aligned.  Its first 256 bytes hold a completion counter that
+ *   MUST be zero before the first call that uses the buffer; every call
+ *   leaves it zero again when it completes, so zero-filling a workspace once
+ *   after allocating it is enough.  Calls that may run at the same time
+ *   (different streams) need different workspaces.  When the required size
+ *   is 0, ws may be NULL.
+ * - Non-finite inputs follow IEEE addition: any NaN, or +Inf together with
+ *   -Inf, gives NaN; otherwise an infinity gives that infinity.
+ * - Inputs that are binary16 subnormals are converted exactly (never
+ *   flushed to zero).
+ */
+#ifndef ARMX_H
+#define ARMX_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum armx_status {
+  ARMX_OK = 0,
+  ARMX_ERR_NULL = -1,      /* a required pointer is NULL                         */
+  ARMX_ERR_ALIGN = -2,     /* x not 16-byte aligned, ws not 256-byte aligned, or */
+                           /* a row pitch that is not a multiple of 8 elements   */
+  ARMX_ERR_CONFIG = -3,    /* block size, chain length, grid or flags invalid    */
+  ARMX_ERR_WORKSPACE = -4, /* ws_bytes smaller than armx_workspace_bytes()       */
+  ARMX_ERR_SHAPE = -5,     /* ld < cols, or a size too large to index            */
+  ARMX_ERR_HIP = -6        /* the HIP runtime reported an error                  */
+} armx_status;
+
+/* Flags for armx_config.flags. */
+#define ARMX_FLAG_PLAIN 0x1u       /* reduce_sum / reduce_rows: the MFMA-free   */
+                                   /* comparison design -- each lane converts  */
+                                   /* its fp16 values and adds them in fp32,   */
+                                   /* then cross-lane and block combines       */
+#define ARMX_FLAG_CACHED_LOADS 0x2u /* read the input with ordinary loads;     */
+                                    /* by default it is streamed with          */
+                                    /* non-temporal loads                      */
+#define ARMX_FLAG_ONE_CHAIN 0x4u   /* reduce_sum: every wavefront runs exactly */
+                                   /* one chain of R tiles, so the grid is     */
+                                   /* ceil(n / (512 R W)) blocks of W waves;   */
+                                   /* without it a persistent grid loops       */
+#define ARMX_FLAG_TWO_PASS 0x8u    /* reduce_sum / fixed order: a second launch */
+                                   /* combines the block results instead of    */
+                                   /* the last block to finish                 */
+
+typedef struct armx_config {
+  int block_threads; /* 0 = default; else 64..1024, a multiple of 64.         */
+                     /* reduce_sum_fixed_order needs a power of two.          */
+  int chain_r;       /* 0 = default; else 1..8.  The number of 16-byte loads  */
+                     /* (and, for the MFMA design, chained MFMAs) per         */
+                     /* wavefront per loop step.                              */
+  int grid_blocks;   /* 0 = automatic; else an upper bound on the grid.       */
+  unsigned flags;    /* ARMX_FLAG_* bits.                                     */
+} armx_config;
+/* Defaults (block_threads, chain_r), measured on MI355X:
+ *   reduce_sum 128, 8; reduce_sum_fixed_order 256, 8; reduce_rows 64, 8.
+ * Automatic persistent grids hold about 2 wavefronts per compute unit for
+ * reduce_sum and reduce_rows (fewer, deeper load streams reach more HBM
+ * bandwidth) and 4 for reduce_sum_fixed_order (more arithmetic per byte). */
+
+/*
+ * reduce_sum -- out[0] = sum of x[0..n), free summation order.
+ *
+ *   "GPU Tensor Cores for fast Arithmetic Reductions", Abstract: the sum of n
+ *   numbers encoded as chained m x m matrix-multiply-accumulates, each chain
+ *   of R kept as a 32-bit float, then all chain results reduced to one
+ *   32-bit float.
+ *
+ * x        device, n binary16 values, contiguous, 16-byte aligned (any
+ *          alignment when n == 0; may be NULL when n == 0).
+ * n        element count, 0 .. 2^40.
+ * out      device, 1 binary32; n == 0 writes +0.0.
+ * ws       device workspace (see conventions), ws_bytes its size.
+ * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
+ *
+ * Each wavefront multiplies an all-ones 16x32 fp16 matrix by 32x16 tiles of
+ * x (one 16-byte load per lane) with v_mfma_f32_16x16x32_f16, chaining R of
+ * them into fp32 accumulators.  The order of additions depends on the
+ * configuration (not on timing): two calls with the same n, configuration
+ * and device give the same bits.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
+ */
+int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
+               const armx_config* cfg, void* stream);
+
+/*
+ * reduce_rows -- out[r] = sum over c < cols of x[r * ld + c], r < rows.
+ *
+ *   A row-segmented form of the same reduction (many independent sums of the
+ *   Abstract of "GPU Tensor Cores for fast Arithmetic Reductions"), free
+ *   summation order inside each row.
+ *
+ * x        device, row-major binary16, row r starts at element r * ld;
+ *          16-byte aligned; ld must be a multiple of 8 when rows > 1.
+ * rows     number of rows (0 writes nothing).
+ * cols     elements summed per row (0 writes +0.0 to every row).
+ * ld       row pitch in elements, ld >= cols.
+ * out      device, rows binary32 values.
+ * ws       unused (armx_workspace_bytes returns 0); may be NULL.
+ * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
+ */
+int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out,
+                void* ws, size_t ws_bytes, const armx_config* cfg, void* stream);
+
+/*
+ * reduce_sum_fixed_order -- out[0] = sum of x[0..n) in one prescribed order.
+ *
+ *   "Taming Bitwise Behavior in GPU Kernels with Tensor Core", Abstract:
+ *   reduction order is the main cause of bit-level differences, and a
+ *   balanced-tree order makes a reduction reproducible.
+ *
+ * The result is the root of the balanced binary tree over x[0..n) padded
+ * with -0.0 to the next power of two, every node the binary32
+ * round-to-nearest-even sum of its two children (leaves are x[i] widened
+ * exactly to binary32).  Each group of 256 consecutive elements is a
+ * complete subtree.  The result is bit-identical for every block size,
+ * chain length, grid and device, and n == 0 gives +0.0.  Only binary32
+ * additions are used (no MFMA and no fused multiply-add).
+ *
+ * x, n, out, ws, ws_bytes as for reduce_sum.  block_threads must be a power
+ * of two.  ARMX_FLAG_PLAIN and ARMX_FLAG_ONE_CHAIN are not accepted.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
+ */
+int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
+                           size_t ws_bytes, const armx_config* cfg, void* stream);
+
+/* Operation codes for armx_workspace_bytes. */
+#define ARMX_OP_SUM 0
+#define ARMX_OP_ROWS 1
+#define ARMX_OP_FIXED 2
+
+/*
+ * armx_workspace_bytes -- bytes of workspace the matching call needs on the
+ * current device with this configuration (0 if none).  `n_or_rows` is n for
+ * ARMX_OP_SUM / ARMX_OP_FIXED and rows for ARMX_OP_ROWS; `cols` is used by
+ * ARMX_OP_ROWS only.  Returns (size_t)-1 for an invalid op or configuration.
+ * Needs no GPU: without a device it assumes 256 compute units.
+ */
+size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
+                            const armx_config* cfg);
+
+/* armx_status_string -- a static, human-readable name for a status code. */
+const char* armx_status_string(int status);
+
+/* armx_version -- ABI version of this header: 1. */
+int armx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ARMX_H */

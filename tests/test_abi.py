@@ -1,0 +1,118 @@
+"""The C ABI library on the CPU: it loads, exports what include/armx.h
+declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import arithmetic_reduction_matrix_amd as armx
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "armx.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order",
+              "armx_workspace_bytes", "armx_status_string", "armx_version"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(armx.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert armx.lib.armx_version() == 1
+    for st in range(0, -7, -1):
+        s = armx.lib.armx_status_string(st).decode()
+        assert s.startswith("ARMX_")
+    assert armx.lib.armx_status_string(-99).decode() == "unknown armx status"
+
+
+def cfg(**kw):
+    return ctypes.byref(armx._config(**kw))
+
+
+FAKE = 1 << 20   # an aligned address; never dereferenced (calls fail first)
+
+
+@pytest.mark.parametrize("fn", ["reduce_sum", "reduce_sum_fixed_order"])
+def test_flat_argument_errors(fn):
+    f = getattr(armx.lib, fn)
+    ws = 1 << 24
+    assert f(None, 10, FAKE, ws, 1 << 20, None, None) == -1          # x NULL
+    assert f(FAKE, 10, None, ws, 1 << 20, None, None) == -1          # out NULL
+    assert f(FAKE + 2, 10, FAKE, ws, 1 << 20, None, None) == -2      # x misaligned
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(block_threads=96), None) == -3
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(block_threads=2048), None) == -3
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(chain_r=9), None) == -3
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(grid_blocks=-1), None) == -3
+    bad_flags = armx.Config(0, 0, 0, 0x100)
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, ctypes.byref(bad_flags), None) == -3
+    assert f(FAKE, 10, FAKE, None, 0, None, None) == -1              # ws needed
+    assert f(FAKE, 10, FAKE, ws + 8, 1 << 20, None, None) == -2      # ws misaligned
+    assert f(FAKE, 10, FAKE, ws, 8, None, None) == -4                # ws too small
+    assert f(FAKE, (1 << 40) + 1, FAKE, ws, 1 << 30, None, None) == -5
+
+
+def test_fixed_order_config_rules():
+    f = armx.lib.reduce_sum_fixed_order
+    ws = 1 << 24
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(block_threads=192), None) == -3   # not 2^k
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(plain=True), None) == -3
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(one_chain=True), None) == -3
+
+
+def test_rows_argument_errors():
+    f = armx.lib.reduce_rows
+    assert f(FAKE, 4, 100, 104, None, None, 0, None, None) == -1      # out NULL
+    assert f(None, 4, 100, 104, FAKE, None, 0, None, None) == -1      # x NULL
+    assert f(FAKE + 2, 4, 100, 104, FAKE, None, 0, None, None) == -2  # misaligned
+    assert f(FAKE, 4, 100, 100, FAKE, None, 0, None, None) == -2      # ld % 8
+    assert f(FAKE, 4, 100, 96, FAKE, None, 0, None, None) == -5       # ld < cols
+    assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(one_chain=True), None) == -3
+    assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(two_pass=True), None) == -3
+    # nothing to do: no rows
+    assert f(None, 0, 100, 104, None, None, 0, None, None) == 0
+
+
+def test_workspace_sizes():
+    # persistent grid: 256 CUs x 2 waves / 2 waves per block = 256 blocks
+    n = 1 << 28
+    assert armx.workspace_bytes(armx.OP_SUM, n) == 256 + 256 * 4
+    assert armx.workspace_bytes(armx.OP_SUM, n, block_threads=64) == 256 + 512 * 4
+    # one chain per wavefront: ceil(n / (512 * R * W)) blocks
+    assert armx.workspace_bytes(armx.OP_SUM, n, one_chain=True, chain_r=4,
+                                block_threads=256) == 256 + (n // (512 * 16)) * 4
+    assert armx.workspace_bytes(armx.OP_SUM, 1000) == 256 + 256       # 1 block, rounded
+    assert armx.workspace_bytes(armx.OP_SUM, 0) == 0
+    assert armx.workspace_bytes(armx.OP_ROWS, 4096, 65536) == 0
+    # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 4 waves -> 256 blocks of
+    # 4 waves x 128 chunks (1024 threads: 64 blocks of 16 waves x 128 chunks)
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26) == 256 + 256 * 4
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=1024) == 256 + 256
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=64) == 256 + 1024 * 4
+    with pytest.raises(armx.ArmxError):
+        armx.workspace_bytes(7, 10)
+    with pytest.raises(armx.ArmxError):
+        armx.workspace_bytes(armx.OP_SUM, 10, chain_r=0, block_threads=100)
+
+
+def test_python_layer_type_checks():
+    import torch
+    with pytest.raises(TypeError):
+        armx.reduce_sum(torch.zeros(8, dtype=torch.float32))
+    with pytest.raises(ValueError):
+        armx.reduce_sum(torch.zeros(8, dtype=torch.float16))      # not on a GPU
+    with pytest.raises(ValueError):
+        armx.reduce_rows(torch.zeros(2, 8, dtype=torch.float16))

@@ -1,0 +1,185 @@
+"""reduce_sum (free order, chained MFMAs against ones; and the MFMA-free
+design) against the exact-sum oracle.  The operation is the arithmetic
+reduction of "GPU Tensor Cores for fast Arithmetic Reductions" (arXiv
+2001.05585, Abstract): fp32 sub-results per chain and an fp32 result."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import arithmetic_reduction_matrix_amd as armx
+import synth_inputs as si
+from oracle import exact_sum
+
+from _parity import bits32, check_free_order, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 2, 7, 8, 9, 255, 256, 257, 511, 512, 513, 2047, 2048, 2049, 4095, 4096, 4097,
+         65536 + 3, (1 << 20) + 37, 3 * (1 << 20) + 1234]
+BLOCKS = [64, 256, 1024]
+CHAINS = [1, 2, 4, 5]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("plain", [False, True])
+def test_sizes_default_config(n, plain):
+    x = si.generate("uniform11", n, seed=n)
+    got = float(armx.reduce_sum(to_dev(x), plain=plain).item())
+    check_free_order(got, exact_sum(x), f"n={n} plain={plain}")
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("r", CHAINS)
+@pytest.mark.parametrize("one_chain", [False, True])
+@pytest.mark.parametrize("plain", [False, True])
+def test_block_chain_matrix(block, r, one_chain, plain):
+    n = (1 << 20) + 4099          # several chains per wave and a ragged tail
+    x = si.generate("uniform01", n, seed=1)
+    got = float(armx.reduce_sum(to_dev(x), block_threads=block, chain_r=r,
+                                one_chain=one_chain, plain=plain).item())
+    check_free_order(got, exact_sum(x), f"block={block} r={r} one_chain={one_chain}")
+
+
+@pytest.mark.parametrize("r", [3, 6, 7, 8])
+@pytest.mark.parametrize("extra", [dict(), dict(cached_loads=True), dict(two_pass=True),
+                                   dict(grid_blocks=7), dict(block_threads=128),
+                                   dict(block_threads=640)])
+def test_other_configs(r, extra):
+    n = (1 << 19) + 333
+    x = si.generate("normal", n, seed=r)
+    got = float(armx.reduce_sum(to_dev(x), chain_r=r, **extra).item())
+    check_free_order(got, exact_sum(x), f"r={r} {extra}")
+
+
+@pytest.mark.parametrize("dist", ["bits_finite", "logu_signed", "normal", "alternating"])
+def test_distributions(dist):
+    n = (1 << 21) + 5
+    x = si.generate(dist, n, seed=77)
+    e = exact_sum(x)
+    for plain in (False, True):
+        got = float(armx.reduce_sum(to_dev(x), plain=plain).item())
+        check_free_order(got, e, f"{dist} plain={plain}")
+
+
+def test_ones_and_ramp_are_exact():
+    # partial sums stay integers far below 2^24 per accumulator, so the fp32
+    # result is exact
+    for n in (1 << 20, (1 << 20) + 17):
+        for dist in ("ones", "ramp2048"):
+            x = si.generate(dist, n)
+            e = exact_sum(x)
+            for plain in (False, True):
+                got = armx.reduce_sum(to_dev(x), plain=plain).item()
+                assert got == float(e.f32), (dist, n, plain, got, e.f32)
+
+
+def test_empty_and_single():
+    z = armx.reduce_sum(torch.empty(0, dtype=torch.float16, device="cuda"))
+    assert z.item() == 0.0 and not math.copysign(1.0, z.item()) < 0
+    for v in (0.5, -3.0, 65504.0, 2.0 ** -24, -(2.0 ** -20)):
+        x = np.array([v], np.float16)
+        assert armx.reduce_sum(to_dev(x)).item() == float(np.float32(x[0]))
+
+
+def test_non_finite():
+    x = si.generate("uniform11", 100_000, seed=3)
+    for pos, vals, expect in [((17,), (np.inf,), math.inf), ((99_999,), (-np.inf,), -math.inf),
+                              ((5, 6), (np.inf, -np.inf), math.nan), ((50_000,), (np.nan,), math.nan)]:
+        y = x.copy()
+        for p, v in zip(pos, vals):
+            y[p] = v
+        for plain in (False, True):
+            got = armx.reduce_sum(to_dev(y), plain=plain).item()
+            if math.isnan(expect):
+                assert math.isnan(got), (pos, plain)
+            else:
+                assert got == expect, (pos, plain, got)
+
+
+def test_run_to_run_determinism_and_workspace_reuse():
+    # the same configuration gives the same bits; alternating grids on one
+    # cached workspace checks that every call leaves its counter at zero
+    x = to_dev(si.generate("uniform11", (1 << 22) + 11, seed=4))
+    first = {}
+    for rep in range(3):
+        for cfg in (dict(), dict(grid_blocks=5), dict(block_threads=1024, chain_r=2),
+                    dict(one_chain=True), dict(plain=True)):
+            key = tuple(sorted(cfg.items()))
+            v = bits32(armx.reduce_sum(x, **cfg).cpu().numpy())
+            assert first.setdefault(key, v) == v, cfg
+
+
+def test_explicit_out_and_workspace():
+    x = si.generate("uniform01", 300_000, seed=9)
+    xd = to_dev(x)
+    need = armx.workspace_bytes(armx.OP_SUM, x.size)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    out = torch.full((1,), 123.0, device="cuda")
+    armx.reduce_sum(xd, out=out, workspace=ws)
+    armx.reduce_sum(xd, out=out, workspace=ws)
+    check_free_order(out.item(), exact_sum(x))
+    with pytest.raises(armx.ArmxError):
+        armx.reduce_sum(xd, workspace=ws[:16])
+
+
+def test_misaligned_view_is_rejected():
+    x = to_dev(si.generate("uniform01", 1000, seed=2))
+    with pytest.raises(armx.ArmxError) as ei:
+        armx.reduce_sum(x[1:])
+    assert ei.value.name == "ARMX_ERR_ALIGN"
+
+
+def test_other_stream():
+    x = si.generate("uniform01", (1 << 20) + 1, seed=6)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = to_dev(x)
+        out = armx.reduce_sum(xd)
+    s.synchronize()
+    check_free_order(out.item(), exact_sum(x))
+
+
+# ---- full-size workloads ---------------------------------------------------
+
+def test_full_2p20_uniform01():
+    x = si.workload("sum_2p20_u01")
+    e = exact_sum(x)
+    for cfg in (dict(), dict(plain=True), dict(one_chain=True, chain_r=4, block_threads=256)):
+        check_free_order(armx.reduce_sum(to_dev(x), **cfg).item(), e, str(cfg))
+
+
+def test_full_2p28_uniform11_bench_configs():
+    x = si.workload("sum_2p28_u11")
+    e = exact_sum(x)
+    xd = to_dev(x)
+    for cfg in (dict(), dict(cached_loads=True), dict(plain=True),
+                dict(one_chain=True, chain_r=4, block_threads=256),
+                dict(one_chain=True, chain_r=5, block_threads=64),
+                dict(one_chain=True, chain_r=1, block_threads=1024)):
+        got = armx.reduce_sum(xd, **cfg).item()
+        rel = check_free_order(got, e, str(cfg))
+        print(f"2^28 {cfg}: got {got!r} exact {e.f64!r} rel {rel:.3e}")
+
+
+def test_full_2p28_all_ones_exact():
+    xd = torch.ones(1 << 28, dtype=torch.float16, device="cuda")
+    for cfg in (dict(), dict(plain=True), dict(one_chain=True)):
+        assert armx.reduce_sum(xd, **cfg).item() == 268435456.0, cfg
+
+
+def test_full_2p30_precision_stress():
+    x = si.workload("sum_2p30_logu")
+    e = exact_sum(x)
+    xd = to_dev(x)
+    del x
+    for cfg in (dict(), dict(plain=True)):
+        got = armx.reduce_sum(xd, **cfg).item()
+        rel = check_free_order(got, e, str(cfg))
+        print(f"2^30 logu {cfg}: got {got!r} exact {e.f64!r} rel {rel:.3e}")
