@@ -55,7 +55,8 @@ class Config(ctypes.Structure):
     """Mirror of ``armx_config``."""
 
     _fields_ = [("block_threads", ctypes.c_int), ("chain_r", ctypes.c_int),
-                ("grid_blocks", ctypes.c_int), ("flags", ctypes.c_uint)]
+                ("grid_blocks", ctypes.c_int), ("flags", ctypes.c_uint),
+                ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
 
 
 def _load() -> ctypes.CDLL:
@@ -82,11 +83,21 @@ def _load() -> ctypes.CDLL:
 lib = _load()
 
 
+def _event_handle(ev) -> int | None:
+    """The hipEvent_t behind a torch.cuda.Event (created on first use)."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()   # torch creates the HIP event lazily
+    return ev.cuda_event
+
+
 def _config(block_threads=0, chain_r=0, grid_blocks=0, plain=False, cached_loads=False,
-            one_chain=False, two_pass=False) -> Config:
+            one_chain=False, two_pass=False, start_event=None, stop_event=None) -> Config:
     flags = ((FLAG_PLAIN if plain else 0) | (FLAG_CACHED_LOADS if cached_loads else 0)
              | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0))
-    return Config(int(block_threads), int(chain_r), int(grid_blocks), flags)
+    return Config(int(block_threads), int(chain_r), int(grid_blocks), flags,
+                  _event_handle(start_event), _event_handle(stop_event))
 
 
 def _check(status: int, what: str) -> None:
@@ -134,22 +145,40 @@ def _check_input(x: torch.Tensor, ndim: int | None, name: str) -> None:
         raise ValueError(f"{name}: expected a {ndim}-D tensor, got {x.dim()}-D")
 
 
+class _on_device:
+    """Makes `dev` the current device for the duration, only if it is not."""
+
+    def __init__(self, dev: torch.device):
+        self.dev = dev.index if dev.index is not None else torch.cuda.current_device()
+        self.prev = None
+
+    def __enter__(self):
+        cur = torch.cuda.current_device()
+        if cur != self.dev:
+            self.prev = cur
+            torch.cuda.set_device(self.dev)
+
+    def __exit__(self, *exc):
+        if self.prev is not None:
+            torch.cuda.set_device(self.prev)
+
+
 def _flat_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config, name: str):
     _check_input(x, None, name)
     if not x.is_contiguous():
         raise ValueError(f"{name}: the input must be contiguous")
     n = x.numel()
     dev = x.device
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if out is None:
             out = torch.empty((), dtype=torch.float32, device=dev)
         elif out.dtype != torch.float32 or out.device != dev or out.numel() < 1:
             raise ValueError(f"{name}: out must be a float32 tensor on {dev}")
-        need = lib.armx_workspace_bytes(op, n, 0, ctypes.byref(cfg))
-        if need == ctypes.c_size_t(-1).value:
-            _check(-3, name)
         if workspace is None:
+            need = lib.armx_workspace_bytes(op, n, 0, ctypes.byref(cfg))
+            if need == ctypes.c_size_t(-1).value:
+                _check(-3, name)
             ws = _workspace(dev, stream, need)
         else:
             ws = workspace
@@ -166,7 +195,9 @@ def reduce_sum(x: torch.Tensor, *, out: torch.Tensor | None = None,
     """Sum of all elements of a contiguous float16 GPU tensor, as float32.
 
     Keyword configuration: block_threads, chain_r, grid_blocks, plain,
-    cached_loads, one_chain, two_pass (see ``include/armx.h``).  A workspace
+    cached_loads, one_chain, two_pass (see ``include/armx.h``), and
+    start_event / stop_event (torch.cuda.Event with timing) which the main
+    kernel's dispatch stamps when it starts and completes.  A workspace
     passed explicitly must be zero-filled before its first use.
     """
     return _flat_call(lib.reduce_sum, OP_SUM, x, out, workspace, _config(**cfg), "reduce_sum")
@@ -190,7 +221,7 @@ def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> t
     ld = x.stride(0) if rows > 1 and cols > 0 else cols
     dev = x.device
     c = _config(**cfg)
-    with torch.cuda.device(dev):
+    with _on_device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if out is None:
             out = torch.empty(rows, dtype=torch.float32, device=dev)

@@ -109,6 +109,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 1; }
+int armx_version(void) { return 2; }
 
 }  // extern "C"

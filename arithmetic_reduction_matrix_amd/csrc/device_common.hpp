@@ -181,27 +181,32 @@ __device__ __forceinline__ void load_chain(const u32x4* __restrict__ base, uint6
   for (int r = 0; r < R; ++r) v[r] = load16<NT>(p + r * 64);
 }
 
-// One chain: R tile steps whose fp32 result starts from zero and is then
-// added (one round-to-nearest-even v_add_f32) into the running per-lane sum
-// `run`.  Keeping each chain's sub-result separate is what holds the error
-// down: a single accumulator carried across many MFMAs grows large, and the
-// MFMA's own accumulation then loses low bits on every step.
-//   MFMA design: lane l's chain result is the sum of column l % 16 of the R
+// One chain: R tile steps whose fp32 result starts from zero; the caller adds
+// it (one round-to-nearest-even v_add_f32) into the running per-lane sum.
+// Keeping each chain's sub-result separate is what holds the error down: a
+// single accumulator carried across many MFMAs grows large, and the MFMA's
+// own accumulation then loses low bits on every step.
+//   MFMA design: lane l's chain value is the sum of column l % 16 of the R
 //   tiles (the same value in all four accumulator registers).
-//   MFMA-free design: lane l's chain result is the sum of its own 8 R values.
+//   MFMA-free design: lane l's chain value is the sum of its own 8 R values.
 template <int R, bool PLAIN>
-__device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
+__device__ __forceinline__ float chain_value(const u32x4 (&v)[R]) {
   if constexpr (PLAIN) {
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) plain_add8(a, b, v[r]);
-    run += a + b;
+    return a + b;
   } else {
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < R; ++r) acc = mfma_ones(acc, v[r]);
-    run += acc[0];
+    return acc[0];
   }
+}
+
+template <int R, bool PLAIN>
+__device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
+  run += chain_value<R, PLAIN>(v);
 }
 
 // Accumulates the full chains c0, c0 + stride, ..., (`iters` of them).
@@ -210,7 +215,9 @@ __device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
 // keeps up to 2R loads in flight and no registers are copied.  Every load in
 // the loop is unconditional -- a branch around a load makes the compiler wait
 // for all loads where the paths join -- so a prefetch past the last chain
-// re-reads that chain (still in L2) and its values are not used.
+// re-reads that chain (still in L2) and its values are not used.  A chain's
+// value is added into `run` one half-step later, after the next loads are
+// issued, so the wait for the MFMA chain's result never delays a prefetch.
 template <int R, bool NT, bool PLAIN>
 __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, uint64_t c0,
                                               uint64_t iters, uint64_t stride, int lane,
@@ -218,15 +225,21 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
   if (iters == 0) return;
   const uint64_t last = c0 + (iters - 1) * stride;
   u32x4 a[R], b[R];
+  float pending = 0.0f;
   load_chain<R, NT>(base, c0, lane, a);
   for (uint64_t j = 0; j < iters; j += 2) {
     load_chain<R, NT>(base, j + 1 < iters ? c0 + (j + 1) * stride : last, lane, b);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
-    chain_step<R, PLAIN>(a, run);
+    run += pending;
+    pending = chain_value<R, PLAIN>(a);
     load_chain<R, NT>(base, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, a);
     __builtin_amdgcn_sched_barrier(0);
-    if (j + 1 < iters) chain_step<R, PLAIN>(b, run);
+    if (j + 1 < iters) {
+      run += pending;
+      pending = chain_value<R, PLAIN>(b);
+    }
   }
+  run += pending;
 }
 
 // The partial chain c (elements [c R 512, end) of a segment of `len` values
@@ -273,14 +286,16 @@ __device__ __forceinline__ float block_sum_lane0(float t, float* red) {
 // Completion ticket.  Thread 0 publishes this block's result in `slot` with
 // an agent-scope atomic store (written through to the level that all XCDs
 // share), waits until that store is complete (s_waitcnt vmcnt(0)), then
-// increments `counter`.  The block whose increment is the last one sees every
-// other block's result through agent-scope atomic loads (load_published).
-// No agent-scope release fence is used: on gfx950 that fence writes back the
-// whole L2 of the XCD, and one per block costs more than the reduction itself.
-// The last block returns the counter to zero for the next call on the same
-// workspace.  Called by every thread; returns true in the last block only.
+// increments `counter`.  The block whose increment is the `arrivals`-th one
+// sees every other participant's result through agent-scope atomic loads
+// (load_published).  No agent-scope release fence is used: on gfx950 that
+// fence writes back the whole L2 of the XCD, and one per block costs more
+// than the reduction itself.  The last block returns the counter to zero for
+// the next call on the same workspace.  Called by every thread; returns true
+// in the last block only.
 __device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
-                                                       unsigned* counter, int* flag) {
+                                                       unsigned* counter, unsigned arrivals,
+                                                       int* flag) {
   if (threadIdx.x == 0) {
     __hip_atomic_store(slot, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -288,7 +303,7 @@ __device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const unsigned prev =
         __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == gridDim.x - 1;
+    const int last = prev == arrivals - 1;
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = last;
   }
@@ -299,6 +314,38 @@ __device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
 // A block result written by publish_and_check_last (or by an earlier kernel).
 __device__ __forceinline__ float load_published(const float* slot) {
   return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Two-level completion.  Blocks form groups of `group` consecutive blocks (a
+// power of two, at most kTicketGroups groups); each group has its own counter
+// and the groups a top counter, so no counter sees more than a few dozen
+// increments and the atomics of different groups proceed in parallel.  The
+// last block of a group combines the group's block results (in index order)
+// into a group result; the last group combines the group results into out[0].
+// `combine(values, count, red)` runs on every thread of the block and returns
+// the combined value in thread 0.  Workspace: counters[0] is the top counter,
+// counters[1 + g] group g's; all start (and end) at zero.
+constexpr unsigned kTicketGroups = 63;
+
+template <class Combine>
+__device__ __forceinline__ void finish_two_level(float value, unsigned* counters,
+                                                 float* partials, float* group_partials,
+                                                 unsigned group, float* out, float* red,
+                                                 int* flag, Combine combine) {
+  const unsigned b = blockIdx.x, G = gridDim.x;
+  const unsigned g = b / group, g0 = g * group;
+  const unsigned in_group = G - g0 < group ? G - g0 : group;
+  const unsigned groups = (G + group - 1) / group;
+  if (!publish_and_check_last(partials + b, value, counters + 1 + g, in_group, flag)) return;
+  const float gv = combine(partials + g0, in_group, red);
+  if (groups == 1) {
+    if (threadIdx.x == 0) out[0] = gv;
+    return;
+  }
+  __syncthreads();
+  if (!publish_and_check_last(group_partials + g, gv, counters, groups, flag)) return;
+  const float v = combine(group_partials, groups, red);
+  if (threadIdx.x == 0) out[0] = v;
 }
 
 }  // namespace dev

@@ -26,7 +26,9 @@
 //  * block = W (a power of two) consecutive wavefront ranges, combined by a
 //    lane_tree over W lanes; the block result is an aligned subtree.
 //  * grid: the block results are combined by the same tree (padded with
-//    -0.0) in the last block to finish, or by a second launch.
+//    -0.0): groups of a power-of-two number of consecutive blocks are
+//    complete subtrees, combined by the last block of each group, and the
+//    group results by the last group (or all of it by a second launch).
 // The chain length R only sets how many chunk loads a wavefront has in
 // flight; it never changes which values are added together.
 #include "device_common.hpp"
@@ -151,37 +153,82 @@ __device__ __forceinline__ void load_group(const u32x4* __restrict__ x, uint64_t
   for (int r = 0; r < R; ++r) v[r] = load16<NT>(p + r * 64);
 }
 
-constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
+constexpr bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
-// Reduces R loaded chunks, items k0 .. k0 + R - 1 of the range (k0 a multiple
-// of R), and appends their nodes in index order.  The R chunk trees are
-// independent and computed first, so their instructions interleave.  When R
-// is a power of two the R nodes form an aligned subtree: it is finished in
-// registers and pushed once at level log2(R).
+// Nodes recorded per group of R chunks: one (the group's subtree root) when R
+// is a power of two -- then a group of R consecutive, R-aligned chunks is a
+// complete subtree -- else one per chunk.
 template <int R>
-__device__ __forceinline__ void reduce_group(const u32x4 (&v)[R], float (&stk)[kStack],
-                                             uint64_t k0) {
+constexpr int kNodesPerGroup = is_pow2(R) ? 1 : R;
+
+// A wavefront's record of node values in index order, kept branch-free: the
+// value (identical in every lane) is selected into lane (count % 64) of a
+// slot register, and the slot register is stored as row count / 64 of this
+// wavefront's LDS array on every record (one conflict-free ds_write).  A new
+// row starts from -0.0, so a partly filled last row is already padded.
+struct NodeLog {
+  float* rows;        // this wavefront's LDS array
+  float slots;        // current row, one node per lane
+  unsigned count;     // nodes recorded
+
+  __device__ __forceinline__ void record(float v, int lane) {
+    const unsigned s = count & 63u;
+    slots = unsigned(lane) == s ? v : (s == 0 ? -0.0f : slots);
+    rows[(count & ~63u) + unsigned(lane)] = slots;
+    ++count;
+  }
+};
+
+// Reduces R loaded chunks (items k0 .. k0 + R - 1, k0 a multiple of R) and
+// records their node(s).  The R chunk trees are independent straight-line
+// code, so they interleave; nothing here branches.
+template <int R>
+__device__ __forceinline__ void reduce_group(const u32x4 (&v)[R], NodeLog& log, int lane) {
   float node[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) node[r] = chunk_node(v[r]);
-  if constexpr ((R & (R - 1)) == 0) {
+  if constexpr (is_pow2(R)) {
 #pragma unroll
     for (int s = 1; s < R; s *= 2) {
 #pragma unroll
       for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
     }
-    counter_push_at<log2_exact(R)>(stk, k0 / R, node[0]);
+    log.record(node[0], lane);
   } else {
 #pragma unroll
-    for (int r = 0; r < R; ++r) counter_push(stk, k0 + r, node[r]);
+    for (int r = 0; r < R; ++r) log.record(node[r], lane);
   }
+}
+
+// Root of the balanced tree over vals[0 .. count) padded with -0.0 to a power
+// of two, by one wavefront (every lane returns it).  Rows of 64 are complete
+// subtrees: each is reduced with lane_tree and its root written back in
+// place (row r's root to vals[r], after row r has been read), until one row
+// is left.
+__device__ float wave_tree(float* vals, unsigned count, int lane) {
+  if (count == 0) return -0.0f;
+  while (count > 64) {
+    const unsigned rows = (count + 63) / 64;
+    for (unsigned r = 0; r < rows; ++r) {
+      const unsigned i = r * 64 + unsigned(lane);
+      const float v = lane_tree_full(i < count ? vals[i] : -0.0f);
+      if (lane == 0) vals[r] = v;
+    }
+    count = rows;
+  }
+  int lv = 0;
+  while ((1u << lv) < count) ++lv;
+  return lane_tree(unsigned(lane) < count ? vals[lane] : -0.0f, lv);
 }
 
 template <int R, bool NT>
 __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x, uint64_t n,
-                                                     int log2c, float* __restrict__ roots,
-                                                     unsigned* __restrict__ counter,
-                                                     float* __restrict__ out, int two_pass) {
+                                                     int log2c, unsigned slots_per_wave,
+                                                     unsigned* __restrict__ counters,
+                                                     float* __restrict__ roots,
+                                                     float* __restrict__ group_roots,
+                                                     unsigned group, float* __restrict__ out,
+                                                     int two_pass) {
   __shared__ float red[16];
   __shared__ int flag;
   const int lane = lane_id();
@@ -191,36 +238,68 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
   const uint64_t span = uint64_t(1) << log2c;
   const uint64_t valid = first >= chunks ? 0 : (chunks - first < span ? chunks - first : span);
 
-  float stk[kStack];
-#pragma unroll
-  for (int j = 0; j < kStack; ++j) stk[j] = -0.0f;
-  // Chunks of this range that lie entirely below n, processed in groups of
-  // R with a software pipeline (ping-pong buffers; every load unconditional,
-  // a prefetch past the last group re-reads that group); then the rest one
-  // by one.
+  // This wavefront's node log in dynamic LDS (`slots_per_wave` floats each).
+  extern __shared__ float node_lds[];
+  NodeLog log{node_lds + unsigned(wave_id()) * slots_per_wave, -0.0f, 0u};
+
+  // Chunks of this range that lie entirely below n, in groups of R, with a
+  // software pipeline (ping-pong buffers, every load unconditional, whole
+  // pairs of groups per iteration, a prefetch past the last group re-reads
+  // it).  The loop body has no branches: a branch there lets the compiler
+  // hoist the second group's reduction above the next prefetch and wait for
+  // every load.
   const uint64_t full = n / 512;
   const uint64_t valid_full = first >= full ? 0 : (full - first < valid ? full - first : valid);
   const uint64_t groups = valid_full / R;
+  uint64_t g = 0;
   if (groups > 0) {
     u32x4 a[R], b[R];
     load_group<R, NT>(x, first, lane, a);
-    for (uint64_t g = 0; g < groups; g += 2) {
-      load_group<R, NT>(x, first + (g + 1 < groups ? g + 1 : groups - 1) * R, lane, b);
+    for (; g + 1 < groups; g += 2) {
+      load_group<R, NT>(x, first + (g + 1) * R, lane, b);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
-      reduce_group<R>(a, stk, g * R);
-      load_group<R, NT>(x, first + (g + 2 < groups ? g + 2 : groups - 1) * R, lane, a);
+      reduce_group<R>(a, log, lane);
+      load_group<R, NT>(x, first + (g + 2 < groups ? g + 2 : g + 1) * R, lane, a);
       __builtin_amdgcn_sched_barrier(0);
-      if (g + 1 < groups) reduce_group<R>(b, stk, (g + 1) * R);
+      reduce_group<R>(b, log, lane);
+    }
+    if (g < groups) {
+      reduce_group<R>(a, log, lane);
+      ++g;
     }
   }
-  for (uint64_t k = groups * R; k < valid; ++k) {
-    const uint64_t gk = first + k;
-    const u32x4 v = gk < full ? load16<NT>(x + gk * 64 + lane)
-                              : load8_masked(reinterpret_cast<const uint16_t*>(x),
-                                             gk * 512 + uint64_t(lane) * 8, n, 0x8000u);
-    counter_push(stk, k, chunk_node(v));
+  // The rest of the range (fewer than R chunks, the last one possibly
+  // straddling n): its leaves past n are -0.0.  For a power-of-two R these
+  // chunks and -0.0 chunks up to R form one more group subtree.
+  if (g * R < valid) {
+    float node[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint64_t k = g * R + r;
+      node[r] = -0.0f;
+      if (k < valid) {
+        const uint64_t gk = first + k;
+        const u32x4 v = gk < full ? load16<NT>(x + gk * 64 + lane)
+                                  : load8_masked(reinterpret_cast<const uint16_t*>(x),
+                                                 gk * 512 + uint64_t(lane) * 8, n, 0x8000u);
+        node[r] = chunk_node(v);
+      }
+    }
+    if constexpr (is_pow2(R)) {
+#pragma unroll
+      for (int s = 1; s < R; s *= 2) {
+#pragma unroll
+        for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
+      }
+      log.record(node[0], lane);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (g * R + r < valid) log.record(node[r], lane);
+      }
+    }
   }
-  const float wave_root = counter_fold(stk, valid);
+  const float wave_root = wave_tree(log.rows, log.count, lane);
 
   // block: W consecutive wavefront subtrees -> one subtree
   __syncthreads();
@@ -242,9 +321,9 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
     if (threadIdx.x == 0) roots[blockIdx.x] = block_root;
     return;
   }
-  if (!publish_and_check_last(roots + blockIdx.x, block_root, counter, &flag)) return;
-  const float root = tree_of_values(roots, gridDim.x, red);
-  if (threadIdx.x == 0) out[0] = root;
+  // groups are aligned power-of-two runs of blocks: complete subtrees
+  finish_two_level(block_root, counters, roots, group_roots, group, out, red, &flag,
+                   tree_of_values);
 }
 
 __global__ __launch_bounds__(1024) void fixed_final_kernel(const float* __restrict__ roots,
@@ -285,15 +364,16 @@ hipError_t launch_fixed(const Plan& plan, const void* x, float* out, void* ws,
   const u32x4* xv = static_cast<const u32x4*>(x);
   uint64_t n = plan.n;
   int log2c = plan.log2_chunks;
-  unsigned* counter = static_cast<unsigned*>(ws);
-  float* roots = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  unsigned slots_per_wave = plan.slots_per_wave;
+  Workspace w = workspace_layout(plan, ws);
+  unsigned group = plan.group;
   int two_pass = (plan.flags & ARMX_FLAG_TWO_PASS) ? 1 : 0;
-  void* args[] = {&xv, &n, &log2c, &roots, &counter, &out, &two_pass};
-  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)),
-                                 args, 0, stream);
+  void* args[] = {&xv, &n, &log2c, &slots_per_wave, &w.counters, &w.partials, &w.group_partials,
+                  &group, &out, &two_pass};
+  hipError_t e = launch_main(plan, fn, args, stream);
   if (e != hipSuccess || !two_pass || plan.grid == 1) return e;
   unsigned count = unsigned(plan.grid);
-  const float* croots = roots;
+  const float* croots = w.partials;
   // the final tree needs a power-of-two block: 1024 threads
   void* fargs[] = {&croots, &count, &out};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fixed_final_kernel), dim3(1), dim3(1024),

@@ -2,11 +2,38 @@
 // the arguments have been checked and a Plan made.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "plan.h"
 
 namespace armx {
+
+// Workspace layout of the reductions with a completion ticket: a 256-byte
+// counter region (top counter, then one per group of blocks), the block
+// results, then the group results.
+struct Workspace {
+  unsigned* counters;
+  float* partials;
+  float* group_partials;
+};
+
+inline Workspace workspace_layout(const Plan& plan, void* ws) {
+  char* base = static_cast<char*>(ws);
+  Workspace w;
+  w.counters = reinterpret_cast<unsigned*>(base);
+  w.partials = reinterpret_cast<float*>(base + kCounterBytes);
+  w.group_partials = reinterpret_cast<float*>(base + kCounterBytes + plan.partials_bytes);
+  return w;
+}
+
+// Launches the main kernel of a plan; the plan's optional events are stamped
+// by the kernel's own dispatch (start and completion).
+inline hipError_t launch_main(const Plan& plan, const void* fn, void** args, hipStream_t stream) {
+  return hipExtLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)), args,
+                            plan.lds_bytes, stream, static_cast<hipEvent_t>(plan.start_event),
+                            static_cast<hipEvent_t>(plan.stop_event), 0);
+}
 
 // out[0] = sum of x[0..plan.n); ws holds the counter and the block results.
 hipError_t launch_sum(const Plan& plan, const void* x, float* out, void* ws, hipStream_t stream);

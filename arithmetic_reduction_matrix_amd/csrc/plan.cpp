@@ -19,6 +19,37 @@ int log2_ceil(uint64_t v) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Blocks of W wavefronts an automatic persistent grid uses: about
+// loads_per_cu / R wavefronts per compute unit, at least one block per unit.
+uint64_t persistent_blocks(const OpDefaults& d, int cu_count, uint64_t W, uint64_t R) {
+  const uint64_t waves_per_cu = (uint64_t(d.loads_per_cu) + R - 1) / R;
+  uint64_t blocks = uint64_t(cu_count) * waves_per_cu / W;
+  if (blocks < uint64_t(cu_count)) blocks = uint64_t(cu_count);
+  return blocks;
+}
+
+// Ticket groups.  Up to kSingleLevelMax blocks use one group: the tail of
+// the kernel then has the fewest serialised memory round trips (measured
+// faster at 256 blocks).  Larger grids use a power-of-two group size near
+// sqrt(grid), so that neither a group counter nor the top counter sees many
+// increments (measured faster at 32768 blocks), with at most kMaxGroups
+// groups.  Sets the workspace sizes.
+constexpr uint64_t kSingleLevelMax = 1024;
+
+void size_ticket(Plan& p) {
+  const uint64_t G = uint64_t(p.grid);
+  uint64_t group = 1;
+  if (G <= kSingleLevelMax) {
+    while (group < G) group <<= 1;
+  } else {
+    while (group * group < G) group <<= 1;
+    while ((G + group - 1) / group > kMaxGroups) group <<= 1;
+  }
+  p.group = unsigned(group);
+  p.partials_bytes = round_up(sizeof(float) * size_t(G), 256);
+  p.ws_bytes = kCounterBytes + p.partials_bytes + 256;
+}
+
 }  // namespace
 
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
@@ -41,6 +72,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   p.waves = c.block_threads / 64;
   p.r = c.chain_r;
   p.flags = c.flags;
+  p.start_event = c.start_event;
+  p.stop_event = c.stop_event;
   const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
 
   if (op == kOpSum) {
@@ -51,8 +84,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     const uint64_t chains = ceil_div(n, kChunk * R);
     uint64_t grid = ceil_div(chains, W);
     if (!(c.flags & ARMX_FLAG_ONE_CHAIN)) {
-      uint64_t resident = uint64_t(cu_count) * uint64_t(d.waves_per_cu) / W;
-      if (resident < 1) resident = 1;
+      const uint64_t resident = persistent_blocks(d, cu_count, W, R);
       if (grid > resident) grid = resident;
     }
     if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) {
@@ -62,7 +94,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     if (grid < 1) grid = 1;
     if (grid > 0x7FFFFFFFull) return ARMX_ERR_SHAPE;
     p.grid = int(grid);
-    p.ws_bytes = kCounterBytes + round_up(sizeof(float) * size_t(grid), 256);
+    size_ticket(p);
   } else if (op == kOpFixed) {
     const uint64_t n = n_or_rows;
     if (n > kMaxN) return ARMX_ERR_SHAPE;
@@ -71,19 +103,30 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.n = n;
     if (n == 0) { *plan = p; return ARMX_OK; }
     const uint64_t chunks = ceil_div(n, kChunk);
-    uint64_t target = uint64_t(cu_count) * uint64_t(d.waves_per_cu) / W;
+    uint64_t target = persistent_blocks(d, cu_count, W, R);
     if (c.grid_blocks > 0 && target > uint64_t(c.grid_blocks)) target = uint64_t(c.grid_blocks);
     if (target > uint64_t(kFixedMaxBlocks)) target = kFixedMaxBlocks;
     if (target < 1) target = 1;
     // every wavefront owns an aligned power-of-two range of chunks, so every
     // wavefront and every block covers a complete subtree of the tree
     int lc = log2_ceil(ceil_div(chunks, W * target));
+    // each wavefront logs one node per R-chunk group (power-of-two R) or per
+    // chunk into LDS, in rows of 64: keep that within kFixedLdsBytes per
+    // block by giving each wavefront fewer chunks (a larger grid)
+    const uint64_t per_node = is_pow2(R) ? R : 1;
+    auto slots = [&](int l) {
+      uint64_t nodes = ceil_div(uint64_t(1) << l, per_node);
+      return (nodes + 63) / 64 * 64;
+    };
+    while (lc > 0 && W * slots(lc) * sizeof(float) > kFixedLdsBytes) --lc;
     if (lc > kFixedMaxLog2Chunks) return ARMX_ERR_SHAPE;
     p.log2_chunks = lc;
+    p.slots_per_wave = unsigned(slots(lc));
+    p.lds_bytes = size_t(W) * slots(lc) * sizeof(float);
     const uint64_t grid = ceil_div(chunks, W << lc);
     if (grid > uint64_t(kFixedMaxBlocks)) return ARMX_ERR_SHAPE;
     p.grid = int(grid);
-    p.ws_bytes = kCounterBytes + round_up(sizeof(float) * size_t(grid), 256);
+    size_ticket(p);
   } else if (op == kOpRows) {
     if (c.flags & (ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS)) return ARMX_ERR_CONFIG;
     const uint64_t rows = n_or_rows;
@@ -95,11 +138,12 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.ld = ld;
     // many rows: one wavefront per row over a persistent grid; few rows: a
     // block per row so that every row still gets W wavefronts
-    uint64_t waves = uint64_t(cu_count) * uint64_t(d.waves_per_cu);
+    const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
+    const uint64_t waves = blocks * W;
     uint64_t grid;
     if (rows >= waves) {
       p.mode = 1;
-      grid = ceil_div(waves, W);
+      grid = blocks;
       if (grid > ceil_div(rows, W)) grid = ceil_div(rows, W);
     } else {
       p.mode = 0;

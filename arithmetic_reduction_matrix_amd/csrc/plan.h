@@ -18,21 +18,29 @@ constexpr uint64_t kTile = 256;
 constexpr int kMaxR = 8;
 constexpr int kMaxWaves = 16;
 // Per-operation defaults (block threads, chain length R) and the number of
-// wavefronts per compute unit an automatic persistent grid aims at.
+// 16-byte loads per lane an automatic persistent grid keeps in flight per
+// compute unit: an HBM stream is latency-bound unless enough bytes are in
+// flight, and measured on MI355X fewer, deeper streams do best, so the grid
+// holds about loads_per_cu / R wavefronts per compute unit (and at least one
+// block per compute unit).
 struct OpDefaults {
   int block;
   int r;
-  int waves_per_cu;
+  int loads_per_cu;
 };
-constexpr OpDefaults kSumDefaults{128, 8, 2};
-constexpr OpDefaults kFixedDefaults{256, 8, 4};
-constexpr OpDefaults kRowsDefaults{64, 8, 2};
+constexpr OpDefaults kSumDefaults{128, 8, 16};
+constexpr OpDefaults kFixedDefaults{256, 8, 32};
+constexpr OpDefaults kRowsDefaults{64, 8, 16};
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;
 // Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.
 constexpr int kFixedMaxLog2Chunks = 24;
-// Workspace: the completion counter sits in the first kCounterBytes.
+// Fixed order keeps each wavefront's node log in LDS: at most this much per block.
+constexpr size_t kFixedLdsBytes = 64 * 1024;
+// Workspace: the completion counters (one top counter and at most
+// kMaxGroups group counters) sit in the first kCounterBytes.
 constexpr size_t kCounterBytes = 256;
+constexpr unsigned kMaxGroups = 63;
 constexpr uint64_t kMaxN = uint64_t(1) << 40;
 
 enum Op { kOpSum = ARMX_OP_SUM, kOpRows = ARMX_OP_ROWS, kOpFixed = ARMX_OP_FIXED };
@@ -45,10 +53,16 @@ struct Plan {
   unsigned flags = 0;
   int log2_chunks = 0;      // fixed order: 2^log2_chunks chunks per wavefront
   int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row
+  unsigned slots_per_wave = 0;  // fixed order: LDS floats of each wavefront's node log
+  size_t lds_bytes = 0;     // dynamic LDS per block
   uint64_t n = 0;           // elements (sum / fixed); columns (rows)
   uint64_t rows = 0;
   uint64_t ld = 0;
   size_t ws_bytes = 0;      // workspace the launch needs
+  size_t partials_bytes = 0;  // block-result region of the workspace
+  unsigned group = 1;       // blocks per completion group (a power of two)
+  void* start_event = nullptr;  // hipEvent_t stamped around the main kernel
+  void* stop_event = nullptr;
 };
 
 // Resolves and checks a configuration for `op`.  `cu_count` is the number of

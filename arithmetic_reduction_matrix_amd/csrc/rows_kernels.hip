@@ -53,9 +53,14 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
       ++pf.k;
     }
   };
-  float run = 0.0f;
-  auto reduce = [&](const u32x4 (&v)[R]) {
-    chain_step<R, PLAIN>(v, run);
+  // A chain's value joins the running sum one half-step later (after the next
+  // loads are issued), so waiting for it never delays a prefetch.
+  float run = 0.0f, pending = 0.0f;
+  bool have_pending = false;
+  auto retire = [&]() {
+    if (!have_pending) return;
+    run += pending;
+    have_pending = false;
     if (++pr.c == cpr) {
       const float total = wave_total<PLAIN>(run);
       if (lane == 0) out[g + pr.k * T] = total;
@@ -63,6 +68,11 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
       pr.c = 0;
       ++pr.k;
     }
+  };
+  auto reduce = [&](const u32x4 (&v)[R]) {
+    retire();
+    pending = chain_value<R, PLAIN>(v);
+    have_pending = true;
   };
   u32x4 a[R], b[R];
   load_chain<R, NT>(ptr(pf), 0, lane, a);
@@ -77,6 +87,7 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < items) reduce(b);
   }
+  retire();
 }
 
 template <int R, bool NT, bool PLAIN>
@@ -157,8 +168,7 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t 
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
   int wave_rows = plan.mode;
   void* args[] = {&xh, &rows, &cols, &ld, &out, &wave_rows};
-  return hipLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)), args, 0,
-                         stream);
+  return launch_main(plan, fn, args, stream);
 }
 
 }  // namespace armx

@@ -22,9 +22,10 @@
 // the wavefront whose turn it is.  With a grid of ceil(chains / W) blocks
 // every wavefront runs exactly one chain; smaller grids loop (persistent).
 // Each block's wavefront totals are combined through LDS into one fp32 block
-// result; the last block to finish reduces the block results in index order
-// (or a second launch does, with ARMX_FLAG_TWO_PASS).  No data atomics are
-// used, so the result depends only on the configuration.
+// result; a two-level completion ticket (groups of blocks, then the groups)
+// lets the last block of each group and then the last group reduce the
+// results in index order (or a second launch does, with ARMX_FLAG_TWO_PASS).
+// No data atomics are used, so the result depends only on the configuration.
 #include "device_common.hpp"
 #include "launch.h"
 
@@ -44,9 +45,11 @@ __device__ float reduce_partials(const float* partials, unsigned count, float* r
 template <int R, bool NT, bool PLAIN>
 __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, uint64_t n,
                                                    uint64_t chains_full,
+                                                   unsigned* __restrict__ counters,
                                                    float* __restrict__ partials,
-                                                   unsigned* __restrict__ counter,
-                                                   float* __restrict__ out, int two_pass) {
+                                                   float* __restrict__ group_partials,
+                                                   unsigned group, float* __restrict__ out,
+                                                   int two_pass) {
   __shared__ float red[16];
   __shared__ int flag;
   const int lane = lane_id();
@@ -72,9 +75,8 @@ __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, 
     if (threadIdx.x == 0) partials[blockIdx.x] = block_total;
     return;
   }
-  if (!publish_and_check_last(partials + blockIdx.x, block_total, counter, &flag)) return;
-  const float total = reduce_partials(partials, gridDim.x, red);
-  if (threadIdx.x == 0) out[0] = total;
+  finish_two_level(block_total, counters, partials, group_partials, group, out, red, &flag,
+                   reduce_partials);
 }
 
 __global__ __launch_bounds__(1024) void final_sum_kernel(const float* __restrict__ partials,
@@ -133,15 +135,15 @@ hipError_t launch_sum(const Plan& plan, const void* x, float* out, void* ws, hip
   const u32x4* xv = static_cast<const u32x4*>(x);
   uint64_t n = plan.n;
   uint64_t chains_full = n / (uint64_t(plan.r) * kChunk);
-  unsigned* counter = static_cast<unsigned*>(ws);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes);
+  Workspace w = workspace_layout(plan, ws);
+  unsigned group = plan.group;
   int two_pass = (plan.flags & ARMX_FLAG_TWO_PASS) ? 1 : 0;
-  void* args[] = {&xv, &n, &chains_full, &partials, &counter, &out, &two_pass};
-  hipError_t e = hipLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)),
-                                 args, 0, stream);
+  void* args[] = {&xv, &n, &chains_full, &w.counters, &w.partials, &w.group_partials, &group,
+                  &out, &two_pass};
+  hipError_t e = launch_main(plan, fn, args, stream);
   if (e != hipSuccess || !two_pass || plan.grid == 1) return e;
   unsigned count = unsigned(plan.grid);
-  const float* cpart = partials;
+  const float* cpart = w.partials;
   void* fargs[] = {&cpart, &count, &out};
   return hipLaunchKernel(reinterpret_cast<const void*>(&final_sum_kernel), dim3(1), dim3(1024),
                          fargs, 0, stream);

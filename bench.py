@@ -1,6 +1,6 @@
 """Benchmark of the fp16 sum-reduction hot path on one MI355X.
 
-One step = one reduce_sum call (chained MFMAs against ones, fp32 partials,
+One step = one reduce_sum call (chained MFMAs against ones, fp32 chain sub-results,
 block combine, completion-ticket final reduce) over n = 2^28 binary16 values
 drawn uniformly from [-1, 1) with seed 2, the input already resident in HBM.
 Two copies of the input are used in turn so that no step reads data the
@@ -8,14 +8,15 @@ previous step left in the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  `value` is elements/s over the timed steps (wall clock
 between two synchronisations); `roofline.achieved` is the algorithmic bytes of
-one launch (2 bytes per element) divided by the average launch time measured
-with HIP events recorded on the stream the kernel runs on.  `cpu_baseline` is
+one launch (2 bytes per element) divided by the average kernel time, measured
+with HIP events that the kernel's own dispatch stamps (hipExtLaunchKernel) on
+the stream it runs on.  `cpu_baseline` is
 the CPU oracle (exact integer sum) timed on this host.  `variants` times the
 other rows of the hot path (MFMA-free design, fixed balanced-tree order, row
 sums, one-chain-per-wavefront grids) on their own workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
-                    [--no-cpu-baseline] [--sweep]
+                    [--no-cpu-baseline] [--sweep] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -103,6 +104,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the block x R matrix (paper-faithful and persistent grids)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy (torch) five times, the "
+                         "known-size reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -129,22 +133,27 @@ def main() -> int:
     out = torch.empty((), dtype=torch.float32, device=dev)
     ws = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device=dev)
 
-    def step(i):
-        armx.reduce_sum(bufs[i & 1], out=out, workspace=ws)
+    # Per-launch timing: HIP events stamped by the kernel's own dispatch packet
+    # (hipExtLaunchKernel), on the stream the kernel runs on.  The handles are
+    # created (first record) before the timed region.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for s_ev, e_ev in evs:
+        s_ev.record()
+        e_ev.record()
+
+    def step(i, ev=(None, None)):
+        armx.reduce_sum(bufs[i & 1], out=out, workspace=ws, start_event=ev[0], stop_event=ev[1])
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
     t0 = time.perf_counter()
-    for i, (s, e) in enumerate(evs):
-        s.record()
-        step(i)
-        e.record()
+    for i in range(args.steps):
+        step(i, evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sorted(s.elapsed_time(e) for s, e in evs)
+    launch_ms = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs)
     avg_ms = sum(launch_ms) / len(launch_ms)
     result = float(out.item())
 
@@ -217,6 +226,15 @@ def main() -> int:
         var["rows_4096x65536_plain"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
         del rbufs
         record["variants"] = var
+
+    if args.copy_calibration:
+        dst = torch.empty_like(bufs[0])
+        for _ in range(5):
+            dst.copy_(bufs[1])
+        torch.cuda.synchronize()
+        record["copy_calibration"] = {"bytes_read": 2 * n, "bytes_written": 2 * n,
+                                      "launches": 5, "kernel": "torch copy_ (fp16, 512 MiB)"}
+        del dst
 
     if args.sweep:
         sweep = {}

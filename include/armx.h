@@ -84,12 +84,17 @@ typedef struct armx_config {
                      /* wavefront per loop step.                              */
   int grid_blocks;   /* 0 = automatic; else an upper bound on the grid.       */
   unsigned flags;    /* ARMX_FLAG_* bits.                                     */
+  void* start_event; /* optional hipEvent_t (NULL = none): stamped by the     */
+  void* stop_event;  /* dispatch packet of the main kernel when it starts and */
+                     /* when it completes (hipExtLaunchKernel), so          */
+                     /* hipEventElapsedTime gives that kernel's own duration */
 } armx_config;
 /* Defaults (block_threads, chain_r), measured on MI355X:
  *   reduce_sum 128, 8; reduce_sum_fixed_order 256, 8; reduce_rows 64, 8.
- * Automatic persistent grids hold about 2 wavefronts per compute unit for
- * reduce_sum and reduce_rows (fewer, deeper load streams reach more HBM
- * bandwidth) and 4 for reduce_sum_fixed_order (more arithmetic per byte). */
+ * Automatic persistent grids hold about 16 / R wavefronts per compute unit
+ * for reduce_sum and reduce_rows (2 at the default R: fewer, deeper load
+ * streams reach more HBM bandwidth) and 32 / R for reduce_sum_fixed_order
+ * (more arithmetic per byte), and at least one block per compute unit. */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.
@@ -176,7 +181,7 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 1. */
+/* armx_version -- ABI version of this header: 2. */
 int armx_version(void);
 
 #ifdef __cplusplus

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 1
+    assert armx.lib.armx_version() == 2
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
@@ -87,21 +87,29 @@ def test_rows_argument_errors():
 
 
 def test_workspace_sizes():
+    # layout: 256-byte counter region + block results (rounded to 256 bytes)
+    # + 256 bytes of group results
+    def ws(grid):
+        return 256 + (4 * grid + 255) // 256 * 256 + 256
     # persistent grid: 256 CUs x 2 waves / 2 waves per block = 256 blocks
     n = 1 << 28
-    assert armx.workspace_bytes(armx.OP_SUM, n) == 256 + 256 * 4
-    assert armx.workspace_bytes(armx.OP_SUM, n, block_threads=64) == 256 + 512 * 4
+    assert armx.workspace_bytes(armx.OP_SUM, n) == ws(256)
+    assert armx.workspace_bytes(armx.OP_SUM, n, block_threads=64) == ws(512)
+    # 1024 threads: at least one block per CU; R = 1: 16 waves per CU
+    assert armx.workspace_bytes(armx.OP_SUM, n, block_threads=1024) == ws(256)
+    assert armx.workspace_bytes(armx.OP_SUM, n, chain_r=1, block_threads=256) == ws(1024)
     # one chain per wavefront: ceil(n / (512 * R * W)) blocks
     assert armx.workspace_bytes(armx.OP_SUM, n, one_chain=True, chain_r=4,
-                                block_threads=256) == 256 + (n // (512 * 16)) * 4
-    assert armx.workspace_bytes(armx.OP_SUM, 1000) == 256 + 256       # 1 block, rounded
+                                block_threads=256) == ws(n // (512 * 16))
+    assert armx.workspace_bytes(armx.OP_SUM, 1000) == ws(1)
     assert armx.workspace_bytes(armx.OP_SUM, 0) == 0
     assert armx.workspace_bytes(armx.OP_ROWS, 4096, 65536) == 0
-    # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 4 waves -> 256 blocks of
-    # 4 waves x 128 chunks (1024 threads: 64 blocks of 16 waves x 128 chunks)
-    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26) == 256 + 256 * 4
-    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=1024) == 256 + 256
-    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=64) == 256 + 1024 * 4
+    # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 32/8 waves -> 256 blocks
+    # of 4 waves x 128 chunks (1024 threads: still one block per CU, 256
+    # blocks of 16 waves x 32 chunks)
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26) == ws(256)
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=1024) == ws(256)
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=64) == ws(1024)
     with pytest.raises(armx.ArmxError):
         armx.workspace_bytes(7, 10)
     with pytest.raises(armx.ArmxError):

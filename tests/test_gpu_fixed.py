@@ -125,3 +125,15 @@ def test_full_2p26_bit_identity_matrix():
     assert set(seen.values()) == {want}, seen
     assert fixed(xd, cached_loads=True) == want
     assert fixed(xd, two_pass=True) == want
+
+
+def test_large_n_node_logs():
+    # 2^30 values: long per-wavefront node logs (per chunk for R = 5, per
+    # group of 8 for R = 8) and several rows of 64 in the wavefront tree
+    x = si.generate("uniform11", 1 << 30, seed=31)
+    want = bits32(fixed_tree_sum(x))
+    xd = to_dev(x)
+    del x
+    for cfg in (dict(), dict(chain_r=5), dict(block_threads=1024, chain_r=1),
+                dict(block_threads=64, chain_r=2)):
+        assert fixed(xd, **cfg) == want, cfg

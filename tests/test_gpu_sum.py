@@ -183,3 +183,16 @@ def test_full_2p30_precision_stress():
         got = armx.reduce_sum(xd, **cfg).item()
         rel = check_free_order(got, e, str(cfg))
         print(f"2^30 logu {cfg}: got {got!r} exact {e.f64!r} rel {rel:.3e}")
+
+
+def test_dispatch_stamped_events():
+    # the main kernel's dispatch stamps the events: a positive duration close
+    # to the wall time of a synchronised call
+    x = to_dev(si.generate("uniform11", 1 << 24, seed=12))
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        out = armx.reduce_sum(x, start_event=s, stop_event=e)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    assert 0.0 < ms < 50.0, ms
+    check_free_order(out.item(), exact_sum(si.generate("uniform11", 1 << 24, seed=12)))
