@@ -89,6 +89,24 @@ __device__ __forceinline__ float add_xor32(float v) {
   return bitsf(int(p[0])) + bitsf(int(p[1]));
 }
 
+// Row-pair sums of two different registers at once.  With 16-lane rows
+// a = [a0 a1 a2 a3] and b = [b0 b1 b2 b3] (each row holding one value),
+// v_permlane16_swap(a, b) exchanges a's odd rows with b's even rows, so the
+// two results are [a0 b0 a2 b2] and [a1 b1 a3 b3] and their sum is
+// [a0+a1, b0+b1, a2+a3, b2+b3].
+__device__ __forceinline__ float pair_rows16(float a, float b) {
+  auto p = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(b), false, false);
+  return bitsf(int(p[0])) + bitsf(int(p[1]));
+}
+
+// Half sums of two different registers at once: with a = [alo ahi] and
+// b = [blo bhi] (32-lane halves), v_permlane32_swap(a, b) gives [alo blo]
+// and [ahi bhi], whose sum is [alo+ahi, blo+bhi].
+__device__ __forceinline__ float pair_halves32(float a, float b) {
+  auto p = __builtin_amdgcn_permlane32_swap(fbits(a), fbits(b), false, false);
+  return bitsf(int(p[0])) + bitsf(int(p[1]));
+}
+
 // ---- fixed pairing ladder ---------------------------------------------------
 //
 // Level j (1-based) adds the values of aligned lane groups of size 2^(j-1)

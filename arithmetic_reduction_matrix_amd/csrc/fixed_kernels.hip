@@ -52,11 +52,53 @@ __device__ __forceinline__ float pair_node(uint32_t w) {
   return r;
 }
 
-// Node of one chunk, from this lane's 8 values; identical in every lane.
-__device__ __forceinline__ float chunk_node(u32x4 t) {
+// Levels 1-7 of one chunk: this lane's 8 values (levels 1-3 in-lane), then
+// lanes ^ 1, ^ 2 and the mirrors within 8 and 16 lanes (levels 4-7).  Every
+// lane of a 16-lane row ends with that row's 128-value node.
+__device__ __forceinline__ float chunk_rows(u32x4 t) {
   const float b0 = pair_node(t[0]) + pair_node(t[1]);
   const float b1 = pair_node(t[2]) + pair_node(t[3]);
-  return lane_tree_full(b0 + b1);
+  return lane_tree(b0 + b1, 4);
+}
+
+// Node of one chunk, from this lane's 8 values; identical in every lane.
+__device__ __forceinline__ float chunk_node(u32x4 t) {
+  return add_xor32(add_xor16(chunk_rows(t)));
+}
+
+// Node of a power-of-two group of R consecutive chunks (an aligned subtree of
+// 512 R values), identical in every lane.  After levels 1-7 each chunk is four
+// row nodes [c0 c1 c2 c3]; the remaining levels pair rows, halves and then
+// chunks, two registers at a time, with the row and half permutes:
+//   level 8  pair_rows16(A, B)     -> [A01 B01 A23 B23]
+//   level 9  pair_halves32(AB, CD) -> [A B C D] (chunk nodes, one per row)
+//   level 10 pair_rows16(ABCD, EFGH) -> [A+B E+F C+D G+H]
+//   ... and so on, each add one node of the balanced tree.
+template <int R>
+__device__ __forceinline__ float group_node(const u32x4 (&v)[R]) {
+  static_assert(R == 2 || R == 4 || R == 8, "packed group tree for R = 2, 4, 8");
+  float rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = chunk_rows(v[r]);
+  if constexpr (R == 2) {
+    const float p = pair_rows16(rows[0], rows[1]);  // [A01 B01 A23 B23]
+    const float q = add_xor32(p);                   // [A B A B]
+    return add_xor16(q);                            // A+B everywhere
+  } else if constexpr (R == 4) {
+    const float p = pair_rows16(rows[0], rows[1]);  // [A01 B01 A23 B23]
+    const float q = pair_rows16(rows[2], rows[3]);  // [C01 D01 C23 D23]
+    const float c = pair_halves32(p, q);            // [A B C D]
+    return add_xor32(add_xor16(c));                 // [A+B . C+D .] -> A+B+C+D
+  } else {
+    const float p0 = pair_rows16(rows[0], rows[1]);
+    const float p1 = pair_rows16(rows[2], rows[3]);
+    const float p2 = pair_rows16(rows[4], rows[5]);
+    const float p3 = pair_rows16(rows[6], rows[7]);
+    const float c0 = pair_halves32(p0, p1);         // [A B C D]
+    const float c1 = pair_halves32(p2, p3);         // [E F G H]
+    const float d = pair_rows16(c0, c1);            // [A+B E+F C+D G+H]
+    return add_xor16(add_xor32(d));                 // [AB+CD EF+GH ..] -> all eight
+  }
 }
 
 // Binary counter over aligned subtrees.  Pushing item g at level L (a node
@@ -180,21 +222,18 @@ struct NodeLog {
 };
 
 // Reduces R loaded chunks (items k0 .. k0 + R - 1, k0 a multiple of R) and
-// records their node(s).  The R chunk trees are independent straight-line
-// code, so they interleave; nothing here branches.
+// records their node(s): the group's subtree root for R = 2, 4, 8, else one
+// node per chunk.  Straight-line code; nothing here branches.
 template <int R>
 __device__ __forceinline__ void reduce_group(const u32x4 (&v)[R], NodeLog& log, int lane) {
-  float node[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) node[r] = chunk_node(v[r]);
-  if constexpr (is_pow2(R)) {
-#pragma unroll
-    for (int s = 1; s < R; s *= 2) {
-#pragma unroll
-      for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
-    }
-    log.record(node[0], lane);
+  if constexpr (R == 1) {
+    log.record(chunk_node(v[0]), lane);
+  } else if constexpr (is_pow2(R)) {
+    log.record(group_node<R>(v), lane);
   } else {
+    float node[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) node[r] = chunk_node(v[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) log.record(node[r], lane);
   }

@@ -29,7 +29,7 @@ struct OpDefaults {
   int loads_per_cu;
 };
 constexpr OpDefaults kSumDefaults{128, 8, 16};
-constexpr OpDefaults kFixedDefaults{256, 8, 32};
+constexpr OpDefaults kFixedDefaults{128, 8, 16};
 constexpr OpDefaults kRowsDefaults{64, 8, 16};
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;

@@ -90,11 +90,10 @@ typedef struct armx_config {
                      /* hipEventElapsedTime gives that kernel's own duration */
 } armx_config;
 /* Defaults (block_threads, chain_r), measured on MI355X:
- *   reduce_sum 128, 8; reduce_sum_fixed_order 256, 8; reduce_rows 64, 8.
+ *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8.
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
- * for reduce_sum and reduce_rows (2 at the default R: fewer, deeper load
- * streams reach more HBM bandwidth) and 32 / R for reduce_sum_fixed_order
- * (more arithmetic per byte), and at least one block per compute unit. */
+ * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth),
+ * and at least one block per compute unit. */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.

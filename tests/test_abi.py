@@ -104,12 +104,12 @@ def test_workspace_sizes():
     assert armx.workspace_bytes(armx.OP_SUM, 1000) == ws(1)
     assert armx.workspace_bytes(armx.OP_SUM, 0) == 0
     assert armx.workspace_bytes(armx.OP_ROWS, 4096, 65536) == 0
-    # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 32/8 waves -> 256 blocks
-    # of 4 waves x 128 chunks (1024 threads: still one block per CU, 256
-    # blocks of 16 waves x 32 chunks)
+    # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 16/8 waves -> 256 blocks
+    # of 2 waves x 256 chunks (1024 threads: still one block per CU, 256
+    # blocks of 16 waves x 32 chunks; 64 threads: 512 blocks of 256 chunks)
     assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26) == ws(256)
     assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=1024) == ws(256)
-    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=64) == ws(1024)
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 26, block_threads=64) == ws(512)
     with pytest.raises(armx.ArmxError):
         armx.workspace_bytes(7, 10)
     with pytest.raises(armx.ArmxError):
