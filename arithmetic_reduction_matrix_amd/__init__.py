@@ -16,6 +16,8 @@ Entry points (same names as the C ABI):
 * ``reduce_sum_fixed_order(x)`` -- sum in one prescribed balanced-tree order,
   bit-identical for every configuration ("Taming Bitwise Behavior in GPU
   Kernels with Tensor Core", arXiv 2609.11356, Abstract).
+* ``reduce_rows_fixed_order(x)`` -- the same order per row: each row's bits
+  depend on that row only (batch invariance, same Abstract).
 """
 from __future__ import annotations
 
@@ -26,14 +28,15 @@ import threading
 import torch
 
 __all__ = [
-    "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "workspace_bytes",
-    "ArmxError", "Config", "LIB_PATH", "OP_SUM", "OP_ROWS", "OP_FIXED",
+    "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
+    "workspace_bytes", "ArmxError", "Config", "LIB_PATH", "OP_SUM", "OP_ROWS", "OP_FIXED",
+    "OP_ROWS_FIXED",
     "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so")
 
-OP_SUM, OP_ROWS, OP_FIXED = 0, 1, 2
+OP_SUM, OP_ROWS, OP_FIXED, OP_ROWS_FIXED = 0, 1, 2, 3
 FLAG_PLAIN, FLAG_CACHED_LOADS, FLAG_ONE_CHAIN, FLAG_TWO_PASS = 0x1, 0x2, 0x4, 0x8
 
 _STATUS = {
@@ -69,7 +72,9 @@ def _load() -> ctypes.CDLL:
     lib.reduce_sum.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_sum_fixed_order.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_rows.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
-    for f in (lib.reduce_sum, lib.reduce_sum_fixed_order, lib.reduce_rows):
+    lib.reduce_rows_fixed_order.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
+    for f in (lib.reduce_sum, lib.reduce_sum_fixed_order, lib.reduce_rows,
+              lib.reduce_rows_fixed_order):
         f.restype = ctypes.c_int
     lib.armx_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, cfgp]
     lib.armx_workspace_bytes.restype = sz
@@ -211,23 +216,34 @@ def reduce_sum_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
                       "reduce_sum_fixed_order")
 
 
-def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> torch.Tensor:
-    """float32 sum of every row of a 2-D float16 GPU tensor whose rows are
-    contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8."""
-    _check_input(x, 2, "reduce_rows")
+def _rows_call(fn, x: torch.Tensor, out, cfg: Config, name: str) -> torch.Tensor:
+    _check_input(x, 2, name)
     rows, cols = x.shape
     if cols > 1 and x.stride(1) != 1:
-        raise ValueError("reduce_rows: rows must be contiguous (stride(1) == 1)")
+        raise ValueError(f"{name}: rows must be contiguous (stride(1) == 1)")
     ld = x.stride(0) if rows > 1 and cols > 0 else cols
     dev = x.device
-    c = _config(**cfg)
     with _on_device(dev):
         stream = torch.cuda.current_stream(dev).cuda_stream
         if out is None:
             out = torch.empty(rows, dtype=torch.float32, device=dev)
         elif out.dtype != torch.float32 or out.device != dev or out.numel() < rows:
-            raise ValueError(f"reduce_rows: out must be a float32 tensor of {rows} on {dev}")
-        st = lib.reduce_rows(x.data_ptr() if x.numel() else None, rows, cols, ld,
-                             out.data_ptr() if rows else None, None, 0, ctypes.byref(c), stream)
-    _check(st, "reduce_rows")
+            raise ValueError(f"{name}: out must be a float32 tensor of {rows} on {dev}")
+        st = fn(x.data_ptr() if x.numel() else None, rows, cols, ld,
+                out.data_ptr() if rows else None, None, 0, ctypes.byref(cfg), stream)
+    _check(st, name)
     return out
+
+
+def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+    """float32 sum of every row of a 2-D float16 GPU tensor whose rows are
+    contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8."""
+    return _rows_call(lib.reduce_rows, x, out, _config(**cfg), "reduce_rows")
+
+
+def reduce_rows_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
+                            **cfg) -> torch.Tensor:
+    """Balanced-tree-order float32 sum of every row (as reduce_rows): row r's
+    bits depend on row r's values only (batch invariant)."""
+    return _rows_call(lib.reduce_rows_fixed_order, x, out, _config(**cfg),
+                      "reduce_rows_fixed_order")

@@ -88,10 +88,29 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, 
   return hip_status(armx::launch_rows(plan, x, out, static_cast<hipStream_t>(stream)));
 }
 
+int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
+                            void* ws, size_t ws_bytes, const armx_config* cfg, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (rows > 0 && !out) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  armx::Plan probe;
+  int st = armx::make_plan(armx::kOpRowsFixed, rows, cols, ld, cfg, 256, &probe);
+  if (st != ARMX_OK) return st;
+  armx::Plan plan;
+  st = armx::make_plan(armx::kOpRowsFixed, rows, cols, ld, cfg,
+                       rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
+  if (st != ARMX_OK) return st;
+  return hip_status(armx::launch_rows_fixed(plan, x, out, static_cast<hipStream_t>(stream)));
+}
+
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_config* cfg) {
   armx::Plan plan;
-  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED) return size_t(-1);
-  const int cus = (op == ARMX_OP_ROWS || n_or_rows == 0) ? 256 : current_cu_count();
+  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED && op != ARMX_OP_ROWS_FIXED)
+    return size_t(-1);
+  const int cus = (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED || n_or_rows == 0)
+                      ? 256 : current_cu_count();
   if (armx::make_plan(op, n_or_rows, cols, cols, cfg, cus, &plan) != ARMX_OK) return size_t(-1);
   return plan.ws_bytes;
 }
@@ -109,6 +128,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 2; }
+int armx_version(void) { return 3; }
 
 }  // extern "C"

@@ -54,8 +54,10 @@ void size_ticket(Plan& p) {
 
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
               const armx_config* cfg, int cu_count, Plan* plan) {
-  const OpDefaults d = op == kOpFixed ? kFixedDefaults : op == kOpRows ? kRowsDefaults
-                                                                      : kSumDefaults;
+  const OpDefaults d = op == kOpFixed       ? kFixedDefaults
+                       : op == kOpRows      ? kRowsDefaults
+                       : op == kOpRowsFixed ? kRowsFixedDefaults
+                                            : kSumDefaults;
   armx_config c{};
   if (cfg) c = *cfg;
   if (c.block_threads == 0) c.block_threads = d.block;
@@ -147,6 +149,48 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
       if (grid > ceil_div(rows, W)) grid = ceil_div(rows, W);
     } else {
       p.mode = 0;
+      grid = rows;
+    }
+    if (grid > (uint64_t(1) << 20)) grid = uint64_t(1) << 20;   // blocks loop over rows
+    if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) grid = uint64_t(c.grid_blocks);
+    if (grid < 1) grid = 1;
+    p.grid = int(grid);
+    p.ws_bytes = 0;
+  } else if (op == kOpRowsFixed) {
+    if (c.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS))
+      return ARMX_ERR_CONFIG;
+    if (!is_pow2(W)) return ARMX_ERR_CONFIG;
+    const uint64_t rows = n_or_rows;
+    if (ld < cols) return ARMX_ERR_SHAPE;
+    if (cols > kMaxN || rows > kMaxN || (rows > 0 && ld > kMaxN / rows)) return ARMX_ERR_SHAPE;
+    if (rows > 1 && cols > 0 && ld % 8) return ARMX_ERR_ALIGN;
+    p.rows = rows;
+    p.n = cols;
+    p.ld = ld;
+    if (rows == 0 || cols == 0) { *plan = p; return ARMX_OK; }
+    const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
+    const uint64_t group_elems = R * kChunk;
+    uint64_t grid;
+    if (is_pow2(R) && cols % group_elems == 0 && cols / group_elems <= 64 &&
+        (rows >= blocks * W || W == 1)) {
+      // flat: a wavefront's rows stream back to back; each row is at most
+      // 64 group subtrees, one per lane of a slot register
+      p.mode = 1;
+      grid = blocks;
+      if (grid > ceil_div(rows, W)) grid = ceil_div(rows, W);
+    } else {
+      // general: a block per row, W wavefronts on aligned power-of-two
+      // chunk ranges, node logs in LDS
+      p.mode = 0;
+      const uint64_t chunks = ceil_div(cols, kChunk);
+      const int lc = log2_ceil(ceil_div(chunks, W));
+      const uint64_t per_node = is_pow2(R) ? R : 1;
+      const uint64_t nodes = ceil_div(uint64_t(1) << lc, per_node);
+      const uint64_t slots = (nodes + 63) / 64 * 64;
+      if (W * slots * sizeof(float) > kFixedLdsBytes) return ARMX_ERR_SHAPE;
+      p.log2_chunks = lc;
+      p.slots_per_wave = unsigned(slots);
+      p.lds_bytes = size_t(W * slots * sizeof(float));
       grid = rows;
     }
     if (grid > (uint64_t(1) << 20)) grid = uint64_t(1) << 20;   // blocks loop over rows

@@ -31,6 +31,7 @@ struct OpDefaults {
 constexpr OpDefaults kSumDefaults{128, 8, 16};
 constexpr OpDefaults kFixedDefaults{128, 8, 16};
 constexpr OpDefaults kRowsDefaults{64, 8, 16};
+constexpr OpDefaults kRowsFixedDefaults{64, 8, 16};
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;
 // Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.
@@ -43,7 +44,12 @@ constexpr size_t kCounterBytes = 256;
 constexpr unsigned kMaxGroups = 63;
 constexpr uint64_t kMaxN = uint64_t(1) << 40;
 
-enum Op { kOpSum = ARMX_OP_SUM, kOpRows = ARMX_OP_ROWS, kOpFixed = ARMX_OP_FIXED };
+enum Op {
+  kOpSum = ARMX_OP_SUM,
+  kOpRows = ARMX_OP_ROWS,
+  kOpFixed = ARMX_OP_FIXED,
+  kOpRowsFixed = ARMX_OP_ROWS_FIXED
+};
 
 struct Plan {
   int op = 0;
@@ -52,7 +58,8 @@ struct Plan {
   int grid = 0;             // blocks launched
   unsigned flags = 0;
   int log2_chunks = 0;      // fixed order: 2^log2_chunks chunks per wavefront
-  int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row
+  int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row;
+                            // fixed-order rows: 1 = flat (cross-row stream), 0 = general
   unsigned slots_per_wave = 0;  // fixed order: LDS floats of each wavefront's node log
   size_t lds_bytes = 0;     // dynamic LDS per block
   uint64_t n = 0;           // elements (sum / fixed); columns (rows)

@@ -10,10 +10,11 @@ Prints ONE JSON line.  `value` is elements/s over the timed steps (wall clock
 between two synchronisations); `roofline.achieved` is the algorithmic bytes of
 one launch (2 bytes per element) divided by the average kernel time, measured
 with HIP events that the kernel's own dispatch stamps (hipExtLaunchKernel) on
-the stream it runs on.  `cpu_baseline` is
+the stream it runs on, on every 8th step of the timed region.  `cpu_baseline` is
 the CPU oracle (exact integer sum) timed on this host.  `variants` times the
 other rows of the hot path (MFMA-free design, fixed balanced-tree order, row
-sums, one-chain-per-wavefront grids) on their own workloads.
+sums, fixed-order row sums, one-chain-per-wavefront grids) on their own
+workloads.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
                     [--no-cpu-baseline] [--sweep] [--copy-calibration]
@@ -100,6 +101,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="stamp start/stop events on every k-th timed step (roofline timing)")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
@@ -134,11 +137,14 @@ def main() -> int:
     ws = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device=dev)
 
     # Per-launch timing: HIP events stamped by the kernel's own dispatch packet
-    # (hipExtLaunchKernel), on the stream the kernel runs on.  The handles are
-    # created (first record) before the timed region.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for s_ev, e_ev in evs:
+    # (hipExtLaunchKernel), on the stream the kernel runs on, for every
+    # `event_every`-th step of the timed region (stamping costs ~4.5 us of
+    # dispatch time per launch, so stamping every step would understate the
+    # wall-clock throughput).  The handles are created before the timed region.
+    stamped = list(range(0, args.steps, args.event_every))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in stamped}
+    for s_ev, e_ev in evs.values():
         s_ev.record()
         e_ev.record()
 
@@ -150,10 +156,10 @@ def main() -> int:
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs.get(i, (None, None)))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs)
+    launch_ms = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs.values())
     avg_ms = sum(launch_ms) / len(launch_ms)
     result = float(out.item())
 
@@ -188,6 +194,7 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "sum_kernel<R=8, non-temporal, MFMA>",
             "launch_ms_avg": avg_ms, "launch_ms_median": launch_ms[len(launch_ms) // 2],
+            "launches_timed": len(launch_ms),
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "kernel_source_sha256_16": kernel_source_hash(),
         },
@@ -224,6 +231,9 @@ def main() -> int:
         ms, med = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout,
                                                                  plain=True), 100)
         var["rows_4096x65536_plain"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(rbufs[i & 1],
+                                                                             out=rout), 200)
+        var["rows_fixed_order_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
         del rbufs
         record["variants"] = var
 

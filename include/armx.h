@@ -90,7 +90,8 @@ typedef struct armx_config {
                      /* hipEventElapsedTime gives that kernel's own duration */
 } armx_config;
 /* Defaults (block_threads, chain_r), measured on MI355X:
- *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8.
+ *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8;
+ *   reduce_rows_fixed_order 64, 8.
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
  * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth),
  * and at least one block per compute unit. */
@@ -162,10 +163,35 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out,
 int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
                            size_t ws_bytes, const armx_config* cfg, void* stream);
 
+/*
+ * reduce_rows_fixed_order -- out[r] = the balanced-tree sum of row r.
+ *
+ *   "Taming Bitwise Behavior in GPU Kernels with Tensor Core", Abstract:
+ *   tile shapes chosen for speed fix the arithmetic and can break batch
+ *   invariance; a balanced-tree order makes a reduction reproducible.
+ *
+ * Row r's result is the root of the balanced binary tree over its cols
+ * values x[r * ld + c] (padded with -0.0 to the next power of two, every
+ * node one binary32 round-to-nearest-even addition) -- exactly
+ * reduce_sum_fixed_order of that row alone.  It therefore depends on the
+ * row's values only: not on rows, on the row's position, on the block size,
+ * chain length or grid (batch invariance).  cols == 0 gives +0.0.
+ *
+ * x, rows, cols, ld, out as for reduce_rows (ld a multiple of 8 when
+ * rows > 1).  ws unused (may be NULL).  block_threads must be a power of
+ * two.  ARMX_FLAG_PLAIN, ARMX_FLAG_ONE_CHAIN and ARMX_FLAG_TWO_PASS are not
+ * accepted.  Rows longer than the LDS node logs allow (about 2^26 values at
+ * R = 8, 2^23 at R = 1) return ARMX_ERR_SHAPE.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
+ */
+int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
+                            void* ws, size_t ws_bytes, const armx_config* cfg, void* stream);
+
 /* Operation codes for armx_workspace_bytes. */
 #define ARMX_OP_SUM 0
 #define ARMX_OP_ROWS 1
 #define ARMX_OP_FIXED 2
+#define ARMX_OP_ROWS_FIXED 3
 
 /*
  * armx_workspace_bytes -- bytes of workspace the matching call needs on the
@@ -180,7 +206,7 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 2. */
+/* armx_version -- ABI version of this header: 3. */
 int armx_version(void);
 
 #ifdef __cplusplus

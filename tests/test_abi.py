@@ -20,7 +20,7 @@ def _declared_functions():
 
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
-    for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order",
+    for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
               "armx_workspace_bytes", "armx_status_string", "armx_version"):
         assert f in names
 
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 2
+    assert armx.lib.armx_version() == 3
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
@@ -84,6 +84,22 @@ def test_rows_argument_errors():
     assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(two_pass=True), None) == -3
     # nothing to do: no rows
     assert f(None, 0, 100, 104, None, None, 0, None, None) == 0
+
+
+def test_rows_fixed_argument_errors():
+    f = armx.lib.reduce_rows_fixed_order
+    assert f(FAKE, 4, 100, 104, None, None, 0, None, None) == -1      # out NULL
+    assert f(None, 4, 100, 104, FAKE, None, 0, None, None) == -1      # x NULL
+    assert f(FAKE + 2, 4, 100, 104, FAKE, None, 0, None, None) == -2  # misaligned
+    assert f(FAKE, 4, 100, 100, FAKE, None, 0, None, None) == -2      # ld % 8
+    assert f(FAKE, 4, 100, 96, FAKE, None, 0, None, None) == -5       # ld < cols
+    assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(block_threads=192), None) == -3
+    assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(plain=True), None) == -3
+    assert f(FAKE, 4, 100, 104, FAKE, None, 0, cfg(two_pass=True), None) == -3
+    # a row too long for the LDS node logs of one block
+    assert f(FAKE, 2, 1 << 30, 1 << 30, FAKE, None, 0, cfg(chain_r=1), None) == -5
+    assert f(None, 0, 100, 104, None, None, 0, None, None) == 0
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 4096, 65536) == 0
 
 
 def test_workspace_sizes():
