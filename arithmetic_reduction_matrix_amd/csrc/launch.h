@@ -27,11 +27,16 @@ inline Workspace workspace_layout(const Plan& plan, void* ws) {
   return w;
 }
 
-// Launches the main kernel of a plan; the plan's optional events are stamped
-// by the kernel's own dispatch (start and completion).
+// Launches the main kernel of a plan.  When the plan carries events they are
+// stamped by the kernel's own dispatch (start and completion) through
+// hipExtLaunchKernel; otherwise it is a plain hipLaunchKernel, which stream
+// capture (HIP graphs) records as an ordinary kernel node.
 inline hipError_t launch_main(const Plan& plan, const void* fn, void** args, hipStream_t stream) {
-  return hipExtLaunchKernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)), args,
-                            plan.lds_bytes, stream, static_cast<hipEvent_t>(plan.start_event),
+  const dim3 grid(unsigned(plan.grid)), block(unsigned(plan.waves * 64));
+  if (!plan.start_event && !plan.stop_event)
+    return hipLaunchKernel(fn, grid, block, args, plan.lds_bytes, stream);
+  return hipExtLaunchKernel(fn, grid, block, args, plan.lds_bytes, stream,
+                            static_cast<hipEvent_t>(plan.start_event),
                             static_cast<hipEvent_t>(plan.stop_event), 0);
 }
 

@@ -1,0 +1,113 @@
+// Host-only fuzz of the launch planner (plan.cpp): random operations, sizes
+// and configurations; every accepted plan must satisfy the invariants the
+// kernels rely on.  Built with AddressSanitizer and UBSan by
+// tests/test_plan_fuzz.py.  Exit status 0 = all invariants held.
+#include <cstdint>
+#include <cstdio>
+#include <random>
+
+#include "plan.h"
+
+using armx::Plan;
+
+static int failures = 0;
+#define EXPECT(cond, ...)                                  \
+  do {                                                     \
+    if (!(cond)) {                                         \
+      ++failures;                                          \
+      std::printf("violated: %s | ", #cond);               \
+      std::printf(__VA_ARGS__);                            \
+      std::printf("\n");                                   \
+    }                                                      \
+  } while (0)
+
+static bool pow2(uint64_t v) { return v && !(v & (v - 1)); }
+static uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+int main(int argc, char** argv) {
+  const int iters = argc > 1 ? std::atoi(argv[1]) : 200000;
+  std::mt19937_64 rng(12345);
+  auto pick_n = [&]() -> uint64_t {
+    switch (rng() % 6) {
+      case 0: return rng() % 64;
+      case 1: return rng() % 100000;
+      case 2: return uint64_t(1) << (rng() % 41);
+      case 3: return (uint64_t(1) << (rng() % 41)) + (rng() % 1000) - 500;
+      case 4: return rng() % (uint64_t(1) << 36);
+      default: return rng();
+    }
+  };
+  int accepted = 0;
+  for (int it = 0; it < iters; ++it) {
+    const int op = int(rng() % 5);  // 4 is not an operation
+    armx_config c{};
+    c.block_threads = (rng() % 4 == 0) ? 0 : int(rng() % 1200);
+    if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
+    c.chain_r = int(rng() % 10);
+    c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
+    c.flags = unsigned(rng() % 32);
+    const uint64_t n = pick_n();
+    const uint64_t cols = pick_n() % (uint64_t(1) << 30);
+    const uint64_t ld = (rng() % 2) ? cols : cols + (rng() % 64);
+    const int cus = int(1 + rng() % 512);
+    Plan p;
+    const int st = armx::make_plan(op, n, cols, ld, &c, cus, &p);
+    if (op == 4) {
+      EXPECT(st == ARMX_ERR_CONFIG, "op 4 accepted");
+      continue;
+    }
+    EXPECT(st <= 0 && st >= ARMX_ERR_HIP, "status %d", st);
+    if (st != ARMX_OK) continue;
+    ++accepted;
+    const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
+    EXPECT(W >= 1 && W <= 16 && R >= 1 && R <= 8, "W %llu R %llu", (unsigned long long)W,
+           (unsigned long long)R);
+    if (op == ARMX_OP_SUM || op == ARMX_OP_FIXED) {
+      if (p.n == 0) continue;
+      EXPECT(p.grid >= 1, "grid %d", p.grid);
+      EXPECT(pow2(p.group), "group %u", p.group);
+      EXPECT(cdiv(uint64_t(p.grid), p.group) <= armx::kMaxGroups, "groups");
+      EXPECT(p.ws_bytes == armx::kCounterBytes + p.partials_bytes + 256, "ws layout");
+      EXPECT(p.partials_bytes >= 4 * uint64_t(p.grid) && p.partials_bytes % 256 == 0, "partials");
+    }
+    if (op == ARMX_OP_SUM) {
+      const uint64_t chains = cdiv(p.n, 512 * R);
+      if (p.flags & ARMX_FLAG_ONE_CHAIN)
+        EXPECT(uint64_t(p.grid) * W >= chains, "one chain: %d blocks x %llu waves < %llu chains",
+               p.grid, (unsigned long long)W, (unsigned long long)chains);
+      EXPECT(uint64_t(p.grid) <= cdiv(chains, W), "more blocks than chains need");
+    }
+    if (op == ARMX_OP_FIXED) {
+      const uint64_t chunks = cdiv(p.n, 512);
+      EXPECT(pow2(W), "fixed W %llu", (unsigned long long)W);
+      EXPECT(p.grid <= armx::kFixedMaxBlocks, "fixed grid %d", p.grid);
+      EXPECT((uint64_t(p.grid) * W << p.log2_chunks) >= chunks, "fixed coverage");
+      EXPECT(((uint64_t(p.grid) - 1) * W << p.log2_chunks) < chunks, "fixed empty block");
+      EXPECT(p.lds_bytes <= armx::kFixedLdsBytes, "lds %zu", p.lds_bytes);
+      EXPECT(p.lds_bytes == W * p.slots_per_wave * sizeof(float), "lds size");
+      EXPECT(p.slots_per_wave % 64 == 0, "slots %u", p.slots_per_wave);
+      const uint64_t per_node = pow2(R) ? R : 1;
+      EXPECT(uint64_t(p.slots_per_wave) >= cdiv(uint64_t(1) << p.log2_chunks, per_node),
+             "slots too few");
+    }
+    if (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED) {
+      EXPECT(p.ld >= p.n, "ld");
+      EXPECT(p.ws_bytes == 0, "rows workspace");
+      if (p.rows == 0 || p.n == 0) continue;
+      EXPECT(p.grid >= 1 && uint64_t(p.grid) <= (uint64_t(1) << 20), "rows grid %d", p.grid);
+      if (p.rows > 1) EXPECT(p.ld % 8 == 0, "pitch");
+    }
+    if (op == ARMX_OP_ROWS_FIXED) {
+      EXPECT(pow2(W), "rows fixed W");
+      if (p.mode == 1) {
+        EXPECT(pow2(R) && p.n % (512 * R) == 0 && p.n / (512 * R) <= 64, "flat shape");
+      } else {
+        EXPECT((W << p.log2_chunks) >= cdiv(p.n, 512), "rows fixed coverage");
+        EXPECT(p.lds_bytes <= armx::kFixedLdsBytes, "rows fixed lds");
+        EXPECT(p.lds_bytes == W * p.slots_per_wave * sizeof(float), "rows fixed lds size");
+      }
+    }
+  }
+  std::printf("plans accepted %d of %d, violations %d\n", accepted, iters, failures);
+  return failures ? 1 : 0;
+}

@@ -1,0 +1,96 @@
+"""Every entry point inside a captured HIP graph (replayed several times with
+eager work and synchronisations between replays, each replay checked against
+an eager call on the same data), and concurrent calls on several streams."""
+import numpy as np
+import pytest
+import torch
+
+import arithmetic_reduction_matrix_amd as armx
+import synth_inputs as si
+from oracle import exact_sum, fixed_tree_sum
+
+from _parity import bits32, check_free_order, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _bits(t):
+    return np.ascontiguousarray(t.cpu().numpy(), dtype=np.float32).view(np.uint32)
+
+
+def test_graph_capture_and_replay():
+    n = (1 << 22) + 5
+    pool = [to_dev(si.generate("uniform11", n, seed=100 + i)) for i in range(5)]
+    rpool = [to_dev(si.generate_rows("normal", 256, 4096, seed=200 + i)) for i in range(5)]
+    x = torch.empty_like(pool[0])
+    m = torch.empty_like(rpool[0])
+    x.copy_(pool[0])
+    m.copy_(rpool[0])
+    o_sum = torch.empty((), dtype=torch.float32, device="cuda")
+    o_fix = torch.empty((), dtype=torch.float32, device="cuda")
+    o_rows = torch.empty(256, dtype=torch.float32, device="cuda")
+    o_rfix = torch.empty(256, dtype=torch.float32, device="cuda")
+    ws_sum = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device="cuda")
+    ws_fix = torch.zeros(armx.workspace_bytes(armx.OP_FIXED, n), dtype=torch.uint8, device="cuda")
+
+    def calls():
+        armx.reduce_sum(x, out=o_sum, workspace=ws_sum)
+        armx.reduce_sum_fixed_order(x, out=o_fix, workspace=ws_fix)
+        armx.reduce_rows(m, out=o_rows)
+        armx.reduce_rows_fixed_order(m, out=o_rfix)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+
+    for rep in range(5):
+        x.copy_(pool[rep])           # eager work between replays
+        m.copy_(rpool[rep])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [_bits(o_sum), _bits(o_fix), _bits(o_rows), _bits(o_rfix)]
+        # eager calls on the same data (own outputs and workspaces)
+        e_sum = armx.reduce_sum(x)
+        e_fix = armx.reduce_sum_fixed_order(x)
+        e_rows = armx.reduce_rows(m)
+        e_rfix = armx.reduce_rows_fixed_order(m)
+        torch.cuda.synchronize()
+        assert np.array_equal(got[0], _bits(e_sum)), rep
+        assert np.array_equal(got[1], _bits(e_fix)), rep
+        assert np.array_equal(got[2], _bits(e_rows)), rep
+        assert np.array_equal(got[3], _bits(e_rfix)), rep
+        if rep in (0, 4):
+            xh = pool[rep].cpu().numpy()
+            assert got[1][()] == bits32(fixed_tree_sum(xh))
+            check_free_order(float(o_sum.item()), exact_sum(xh), f"replay {rep}")
+
+
+def test_concurrent_streams():
+    n = (1 << 21) + 333
+    data = [si.generate("uniform11", n, seed=300 + i) for i in range(4)]
+    xs = [to_dev(d) for d in data]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    outs, fixed = [None] * 4, [None] * 4
+    for i, s in enumerate(streams):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                outs[i] = armx.reduce_sum(xs[i])
+                fixed[i] = armx.reduce_sum_fixed_order(xs[i])
+    torch.cuda.synchronize()
+    for i in range(4):
+        check_free_order(float(outs[i].item()), exact_sum(data[i]), f"stream {i}")
+        assert _bits(fixed[i])[()] == bits32(fixed_tree_sum(data[i]))
