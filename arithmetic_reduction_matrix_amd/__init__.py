@@ -11,13 +11,17 @@ Entry points (same names as the C ABI):
 * ``reduce_sum(x)`` -- sum of a float16 tensor as a 0-dim float32 tensor, by
   chained MFMAs against an all-ones operand ("GPU Tensor Cores for fast
   Arithmetic Reductions", arXiv 2001.05585, Abstract); ``plain=True`` selects
-  the MFMA-free comparison design.
+  the MFMA-free comparison design, ``mma_levels=True`` the recursive form in
+  which every level reduces chains with MFMAs only, one launch per level.
 * ``reduce_rows(x)`` -- float32 sum of every row of a 2-D float16 tensor.
 * ``reduce_sum_fixed_order(x)`` -- sum in one prescribed balanced-tree order,
   bit-identical for every configuration ("Taming Bitwise Behavior in GPU
   Kernels with Tensor Core", arXiv 2609.11356, Abstract).
 * ``reduce_rows_fixed_order(x)`` -- the same order per row: each row's bits
   depend on that row only (batch invariance, same Abstract).
+* ``reduce_sum_exact(x)`` -- the correctly rounded float32 of the exact sum
+  (and, with ``fixed=``, the exact sum as a 128-bit count of 2^-24), the
+  same bits for every configuration.
 """
 from __future__ import annotations
 
@@ -29,15 +33,16 @@ import torch
 
 __all__ = [
     "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
-    "workspace_bytes", "ArmxError", "Config", "LIB_PATH", "OP_SUM", "OP_ROWS", "OP_FIXED",
-    "OP_ROWS_FIXED",
-    "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS",
+    "reduce_sum_exact", "fixed_to_int", "workspace_bytes", "ArmxError", "Config", "LIB_PATH",
+    "OP_SUM", "OP_ROWS", "OP_FIXED", "OP_ROWS_FIXED", "OP_EXACT",
+    "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS", "FLAG_MMA_LEVELS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so")
 
-OP_SUM, OP_ROWS, OP_FIXED, OP_ROWS_FIXED = 0, 1, 2, 3
+OP_SUM, OP_ROWS, OP_FIXED, OP_ROWS_FIXED, OP_EXACT = 0, 1, 2, 3, 4
 FLAG_PLAIN, FLAG_CACHED_LOADS, FLAG_ONE_CHAIN, FLAG_TWO_PASS = 0x1, 0x2, 0x4, 0x8
+FLAG_MMA_LEVELS = 0x10
 
 _STATUS = {
     0: "ARMX_OK", -1: "ARMX_ERR_NULL", -2: "ARMX_ERR_ALIGN", -3: "ARMX_ERR_CONFIG",
@@ -73,8 +78,9 @@ def _load() -> ctypes.CDLL:
     lib.reduce_sum_fixed_order.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_rows.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_rows_fixed_order.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
+    lib.reduce_sum_exact.argtypes = [vp, sz, vp, vp, vp, sz, cfgp, vp]
     for f in (lib.reduce_sum, lib.reduce_sum_fixed_order, lib.reduce_rows,
-              lib.reduce_rows_fixed_order):
+              lib.reduce_rows_fixed_order, lib.reduce_sum_exact):
         f.restype = ctypes.c_int
     lib.armx_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, cfgp]
     lib.armx_workspace_bytes.restype = sz
@@ -98,9 +104,11 @@ def _event_handle(ev) -> int | None:
 
 
 def _config(block_threads=0, chain_r=0, grid_blocks=0, plain=False, cached_loads=False,
-            one_chain=False, two_pass=False, start_event=None, stop_event=None) -> Config:
+            one_chain=False, two_pass=False, mma_levels=False, start_event=None,
+            stop_event=None) -> Config:
     flags = ((FLAG_PLAIN if plain else 0) | (FLAG_CACHED_LOADS if cached_loads else 0)
-             | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0))
+             | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0)
+             | (FLAG_MMA_LEVELS if mma_levels else 0))
     return Config(int(block_threads), int(chain_r), int(grid_blocks), flags,
                   _event_handle(start_event), _event_handle(stop_event))
 
@@ -168,7 +176,8 @@ class _on_device:
             torch.cuda.set_device(self.prev)
 
 
-def _flat_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config, name: str):
+def _flat_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config, name: str,
+               fixed=None):
     _check_input(x, None, name)
     if not x.is_contiguous():
         raise ValueError(f"{name}: the input must be contiguous")
@@ -189,8 +198,16 @@ def _flat_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config, name: 
             ws = workspace
         ws_ptr = ws.data_ptr() if ws is not None else None
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-        st = fn(x.data_ptr() if n else None, n, out.data_ptr(), ws_ptr, ws_bytes,
-                ctypes.byref(cfg), stream)
+        if op == OP_EXACT:
+            if fixed is not None and (fixed.dtype != torch.int64 or fixed.device != dev
+                                      or fixed.numel() < 2 or not fixed.is_contiguous()):
+                raise ValueError(f"{name}: fixed must be a contiguous int64 tensor of 2 on {dev}")
+            st = fn(x.data_ptr() if n else None, n, out.data_ptr(),
+                    fixed.data_ptr() if fixed is not None else None, ws_ptr, ws_bytes,
+                    ctypes.byref(cfg), stream)
+        else:
+            st = fn(x.data_ptr() if n else None, n, out.data_ptr(), ws_ptr, ws_bytes,
+                    ctypes.byref(cfg), stream)
     _check(st, name)
     return out
 
@@ -200,9 +217,10 @@ def reduce_sum(x: torch.Tensor, *, out: torch.Tensor | None = None,
     """Sum of all elements of a contiguous float16 GPU tensor, as float32.
 
     Keyword configuration: block_threads, chain_r, grid_blocks, plain,
-    cached_loads, one_chain, two_pass (see ``include/armx.h``), and
-    start_event / stop_event (torch.cuda.Event with timing) which the main
-    kernel's dispatch stamps when it starts and completes.  A workspace
+    cached_loads, one_chain, two_pass, mma_levels (see ``include/armx.h``),
+    and start_event / stop_event (torch.cuda.Event with timing) which the
+    main kernel's dispatch stamps when it starts and completes (with
+    mma_levels: the first level's start and the last level's completion).  A workspace
     passed explicitly must be zero-filled before its first use.
     """
     return _flat_call(lib.reduce_sum, OP_SUM, x, out, workspace, _config(**cfg), "reduce_sum")
@@ -214,6 +232,25 @@ def reduce_sum_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
     the same bits for every configuration."""
     return _flat_call(lib.reduce_sum_fixed_order, OP_FIXED, x, out, workspace, _config(**cfg),
                       "reduce_sum_fixed_order")
+
+
+def reduce_sum_exact(x: torch.Tensor, *, out: torch.Tensor | None = None,
+                     fixed: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+    """The float32 nearest (ties to even) to the exact sum of a contiguous
+    float16 GPU tensor; the same bits for every configuration.  If ``fixed``
+    (an int64 GPU tensor of 2) is given, the exact sum is also written there
+    as a 128-bit count of 2^-24 (low word, high word); ``fixed_to_int``
+    turns it into a Python int."""
+    return _flat_call(lib.reduce_sum_exact, OP_EXACT, x, out, workspace, _config(**cfg),
+                      "reduce_sum_exact", fixed=fixed)
+
+
+def fixed_to_int(fixed) -> int:
+    """The 128-bit count written by reduce_sum_exact (two int64 words, low
+    first) as a Python int."""
+    lo, hi = (int(v) for v in fixed.reshape(-1)[:2].tolist())
+    return (hi << 64) + (lo & ((1 << 64) - 1))
 
 
 def _rows_call(fn, x: torch.Tensor, out, cfg: Config, name: str) -> torch.Tensor:

@@ -20,8 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libarmx.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["sum_kernels.hip", "fixed_kernels.hip", "rows_kernels.hip",
-               "rows_fixed_kernels.hip"]
+HIP_SOURCES = ["sum_kernels.hip", "fixed_kernels.hip", "rows_kernels.hip", "exact_kernels.hip",
+               "rows_fixed_kernels.hip", "levels_kernels.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -64,6 +64,8 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
   armx::Plan plan;
   int st = prepare_flat(armx::kOpSum, x, n, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
+  if (plan.flags & ARMX_FLAG_MMA_LEVELS)
+    return hip_status(armx::launch_levels(plan, x, out, ws, static_cast<hipStream_t>(stream)));
   return hip_status(armx::launch_sum(plan, x, out, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -73,6 +75,16 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws, size_t
   int st = prepare_flat(armx::kOpFixed, x, n, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
   return hip_status(armx::launch_fixed(plan, x, out, ws, static_cast<hipStream_t>(stream)));
+}
+
+int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, void* ws,
+                     size_t ws_bytes, const armx_config* cfg, void* stream) {
+  armx::Plan plan;
+  int st = prepare_flat(armx::kOpExact, x, n, out, ws, ws_bytes, cfg, &plan);
+  if (st != ARMX_OK) return st;
+  if (out_fixed && !aligned(out_fixed, 8)) return ARMX_ERR_ALIGN;
+  return hip_status(
+      armx::launch_exact(plan, x, out, out_fixed, ws, static_cast<hipStream_t>(stream)));
 }
 
 int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, void* ws,
@@ -107,7 +119,8 @@ int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, 
 
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_config* cfg) {
   armx::Plan plan;
-  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED && op != ARMX_OP_ROWS_FIXED)
+  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED &&
+      op != ARMX_OP_ROWS_FIXED && op != ARMX_OP_EXACT)
     return size_t(-1);
   const int cus = (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED || n_or_rows == 0)
                       ? 256 : current_cu_count();
@@ -128,6 +141,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 3; }
+int armx_version(void) { return 5; }
 
 }  // extern "C"

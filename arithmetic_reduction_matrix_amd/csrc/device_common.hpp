@@ -301,21 +301,21 @@ __device__ __forceinline__ float block_sum_lane0(float t, float* red) {
   return v;
 }
 
-// Completion ticket.  Thread 0 publishes this block's result in `slot` with
-// an agent-scope atomic store (written through to the level that all XCDs
-// share), waits until that store is complete (s_waitcnt vmcnt(0)), then
+// Completion ticket.  Thread 0 publishes this block's result with `publish`
+// (agent-scope atomic stores, written through to the level that all XCDs
+// share), waits until those stores are complete (s_waitcnt vmcnt(0)), then
 // increments `counter`.  The block whose increment is the `arrivals`-th one
-// sees every other participant's result through agent-scope atomic loads
-// (load_published).  No agent-scope release fence is used: on gfx950 that
-// fence writes back the whole L2 of the XCD, and one per block costs more
-// than the reduction itself.  The last block returns the counter to zero for
-// the next call on the same workspace.  Called by every thread; returns true
-// in the last block only.
-__device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
-                                                       unsigned* counter, unsigned arrivals,
-                                                       int* flag) {
+// sees every other participant's result through agent-scope atomic loads.
+// No agent-scope release fence is used: on gfx950 that fence writes back the
+// whole L2 of the XCD, and one per block costs more than the reduction
+// itself.  The last block returns the counter to zero for the next call on
+// the same workspace.  Called by every thread; returns true in the last block
+// only.
+template <class Publish>
+__device__ __forceinline__ bool publish_with_ticket(Publish publish, unsigned* counter,
+                                                    unsigned arrivals, int* flag) {
   if (threadIdx.x == 0) {
-    __hip_atomic_store(slot, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    publish();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), other counters untouched
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -327,6 +327,15 @@ __device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
   }
   __syncthreads();
   return *flag != 0;
+}
+
+// The ticket for one fp32 block result stored in `slot`.
+__device__ __forceinline__ bool publish_and_check_last(float* slot, float value,
+                                                       unsigned* counter, unsigned arrivals,
+                                                       int* flag) {
+  return publish_with_ticket(
+      [&] { __hip_atomic_store(slot, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+      counter, arrivals, flag);
 }
 
 // A block result written by publish_and_check_last (or by an earlier kernel).

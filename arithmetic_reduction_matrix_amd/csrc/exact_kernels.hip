@@ -1,0 +1,321 @@
+// Exact, order-free sum: out = the binary32 nearest (ties to even) to the
+// real sum of x[0..n), and optionally that sum itself as a 128-bit integer
+// count of 2^-24.
+//
+// Every finite binary16 value is an integer multiple of 2^-24 below 2^16 in
+// magnitude, so the sum is an integer count of 2^-24 units, and integer
+// addition is associative: every grouping of the additions gives the same
+// total, whatever the block size, chain length, grid or device.  The
+// kernel keeps every step exact:
+//  * per lane and chain (R loads, 8 R values) the values are widened to
+//    binary64 and added; every partial sum is a multiple of 2^-24 below
+//    8 R 2^16 <= 2^22, which a 53-bit significand holds exactly;
+//  * the chain total t = s 2^24 (an integer below 2^46) is split into two
+//    limbs, t = h 2^32 + l with 0 <= l < 2^32, and each limb is added into
+//    its own 64-bit integer accumulator -- numbers carried as narrow
+//    components with fixed weights (1 and 2^32) and recombined exactly at the
+//    end, the limb representation of "AWE: Adaptive Weight Encoding for Exact
+//    Integer Matrix Products with Fewer GEMMs on FP4 Tensor Cores" (arXiv
+//    2609.24519, Abstract) applied to a sum; neither accumulator can
+//    overflow for n <= 2^40;
+//  * wavefront, block and grid combines add these integers, folding the low
+//    limb's carries into the high one so every term stays below 2^32; the
+//    last block (completion ticket) rounds the 128-bit total once.
+// No MFMA: the operation is bound by HBM bandwidth, and feeding an integer
+// MFMA would first need every value split into 8-bit limbs, which costs more
+// vector instructions per value than the binary64 additions do.
+//
+// Non-finite inputs: a chain whose binary64 sum is not finite sets a flag
+// (+Inf, -Inf or NaN) instead of adding to the integers; the result follows
+// IEEE addition (NaN if any NaN or both infinities, else the infinity), and
+// the 128-bit output is then 0.
+#include "device_common.hpp"
+#include "launch.h"
+
+namespace armx {
+namespace {
+
+using namespace dev;
+
+constexpr unsigned kPosInf = 1, kNegInf = 2, kNaN = 4;
+
+// A partial sum: hi 2^32 + lo units of 2^-24, plus the non-finite flags.
+struct Exact {
+  int64_t hi;
+  uint64_t lo;
+  unsigned flags;
+};
+
+// Moves the carries of lo into hi, leaving 0 <= lo < 2^32.
+__device__ __forceinline__ void fold(Exact& a) {
+  a.hi += int64_t(a.lo >> 32);
+  a.lo &= 0xFFFFFFFFull;
+}
+
+template <int R>
+__device__ __forceinline__ void add_chain(const u32x4 (&v)[R], Exact& a) {
+  double s0 = 0.0, s1 = 0.0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      s0 += double(lo_f32(v[r][w]));
+      s1 += double(hi_f32(v[r][w]));
+    }
+  }
+  const double s = s0 + s1;
+  const bool finite = __builtin_isfinite(s);
+  a.flags |= finite ? 0u : (s != s ? kNaN : (s > 0.0 ? kPosInf : kNegInf));
+  const double t = finite ? s * 0x1p24 : 0.0;
+  const double h = __builtin_floor(t * 0x1p-32);
+  const double l = __builtin_fma(-h, 0x1p32, t);
+  a.hi += int64_t(int(h));
+  a.lo += uint64_t(unsigned(l));
+}
+
+// The full chains c0, c0 + stride, ... (`iters` of them), with the load
+// pipeline of the free-order kernel: the next chain's loads are issued before
+// the current chain's additions, ping-pong buffers, clamped prefetch.
+template <int R, bool NT>
+__device__ __forceinline__ void stream_exact(const u32x4* __restrict__ x, uint64_t c0,
+                                             uint64_t iters, uint64_t stride, int lane,
+                                             Exact& a) {
+  if (iters == 0) return;
+  const uint64_t last = c0 + (iters - 1) * stride;
+  u32x4 p[R], q[R];
+  load_chain<R, NT>(x, c0, lane, p);
+  const uint64_t pairs = iters / 2;
+  for (uint64_t k = 0; k < pairs; ++k) {
+    const uint64_t j = 2 * k;
+    load_chain<R, NT>(x, c0 + (j + 1) * stride, lane, q);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the additions
+    add_chain<R>(p, a);
+    load_chain<R, NT>(x, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, p);
+    __builtin_amdgcn_sched_barrier(0);
+    add_chain<R>(q, a);
+  }
+  if (iters & 1) add_chain<R>(p, a);  // p holds the last chain
+}
+
+// Sum over the 64 lanes (every lane gets it); any order, the sums are exact.
+__device__ __forceinline__ Exact wave_exact(Exact a) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    a.hi += int64_t(__shfl_xor((long long)a.hi, m));
+    a.lo += uint64_t(__shfl_xor((unsigned long long)a.lo, m));
+    a.flags |= unsigned(__shfl_xor(int(a.flags), m));
+  }
+  fold(a);
+  return a;
+}
+
+// Sum over the block's wavefronts (lane 0's values); valid in wavefront 0.
+struct ExactLds {
+  int64_t hi[16];
+  uint64_t lo[16];
+  unsigned flags[16];
+};
+
+__device__ __forceinline__ Exact block_exact(Exact a, ExactLds& s) {
+  __syncthreads();  // s may still be read by a previous call
+  if (lane_id() == 0) {
+    s.hi[wave_id()] = a.hi;
+    s.lo[wave_id()] = a.lo;
+    s.flags[wave_id()] = a.flags;
+  }
+  __syncthreads();
+  Exact r{0, 0, 0};
+  if (wave_id() == 0) {
+    if (lane_id() < num_waves()) r = Exact{s.hi[lane_id()], s.lo[lane_id()], s.flags[lane_id()]};
+    r = wave_exact(r);
+  }
+  return r;
+}
+
+// A published partial: 4 x 64-bit words (hi, lo, flags, unused).
+constexpr int kRecordWords = 4;
+
+__device__ __forceinline__ void store_record(uint64_t* rec, const Exact& a) {
+  __hip_atomic_store(rec + 0, uint64_t(a.hi), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(rec + 1, a.lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(rec + 2, uint64_t(a.flags), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Sum of `count` published records; valid in wavefront 0.
+__device__ Exact combine_records(const uint64_t* recs, unsigned count, ExactLds& s) {
+  Exact a{0, 0, 0};
+  for (unsigned i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint64_t* r = recs + uint64_t(i) * kRecordWords;
+    a.hi += int64_t(__hip_atomic_load(r + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    a.lo += __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.flags |= unsigned(__hip_atomic_load(r + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  }
+  fold(a);
+  return block_exact(wave_exact(a), s);
+}
+
+// The binary32 nearest to (hi 2^64 + lo) 2^-24 (a 128-bit two's complement
+// count), ties to even; +0.0 for zero.  |value| < 2^57 here, so the result is
+// finite and normal or zero.
+__device__ float round_to_binary32(int64_t hi, uint64_t lo) {
+  const bool neg = hi < 0;
+  unsigned __int128 m = (unsigned __int128)(uint64_t(hi)) << 64 | lo;
+  if (neg) m = ~m + 1;
+  if (m == 0) return 0.0f;
+  const uint64_t mh = uint64_t(m >> 64), ml = uint64_t(m);
+  const int p = mh ? 127 - __builtin_clzll(mh) : 63 - __builtin_clzll(ml);  // top bit
+  uint32_t keep;
+  int e;
+  if (p < 24) {
+    keep = uint32_t(ml);
+    e = -24;
+  } else {
+    const int shift = p - 23;
+    keep = uint32_t(m >> shift);
+    const unsigned __int128 rem = m & ((((unsigned __int128)1) << shift) - 1);
+    const unsigned __int128 half = ((unsigned __int128)1) << (shift - 1);
+    if (rem > half || (rem == half && (keep & 1u))) ++keep;
+    e = shift - 24;
+    if (keep == (1u << 24)) {
+      keep >>= 1;
+      ++e;
+    }
+  }
+  const float r = __builtin_ldexpf(float(keep), e);
+  return neg ? -r : r;
+}
+
+__device__ void finish_exact(Exact a, float* out, int64_t* out_fixed) {
+  fold(a);
+  const uint64_t t_lo = (uint64_t(a.hi) << 32) | a.lo;
+  const int64_t t_hi = a.hi >> 32;
+  float r;
+  if ((a.flags & kNaN) || ((a.flags & kPosInf) && (a.flags & kNegInf))) {
+    r = __builtin_nanf("");
+  } else if (a.flags & kPosInf) {
+    r = __builtin_inff();
+  } else if (a.flags & kNegInf) {
+    r = -__builtin_inff();
+  } else {
+    r = round_to_binary32(t_hi, t_lo);
+  }
+  out[0] = r;
+  if (out_fixed) {
+    out_fixed[0] = a.flags ? 0 : int64_t(t_lo);
+    out_fixed[1] = a.flags ? 0 : t_hi;
+  }
+}
+
+template <int R, bool NT>
+__global__ __launch_bounds__(1024) void exact_kernel(const u32x4* __restrict__ x, uint64_t n,
+                                                     uint64_t chains_full,
+                                                     unsigned* __restrict__ counters,
+                                                     uint64_t* __restrict__ partials,
+                                                     uint64_t* __restrict__ group_partials,
+                                                     unsigned group, float* __restrict__ out,
+                                                     int64_t* __restrict__ out_fixed) {
+  __shared__ ExactLds lds;
+  __shared__ int flag;
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t total_waves = uint64_t(gridDim.x) * W;
+  uint64_t c = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
+
+  Exact a{0, 0, 0};
+  const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
+  stream_exact<R, NT>(x, c, iters, total_waves, lane, a);
+  c += iters * total_waves;
+  if (c == chains_full && chains_full * R * kChunk < n) {
+    // the partial chain at the end: values past n read as +0.0
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
+    u32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint64_t e = (c * R + r) * kChunk + uint64_t(lane) * 8;
+      v[r] = e < n ? load8_masked(xh, e, n, 0u) : u32x4{0u, 0u, 0u, 0u};
+    }
+    add_chain<R>(v, a);
+  }
+  fold(a);
+  const Exact block_total = block_exact(wave_exact(a), lds);
+
+  if (gridDim.x == 1) {
+    if (threadIdx.x == 0) finish_exact(block_total, out, out_fixed);
+    return;
+  }
+  const unsigned b = blockIdx.x, G = gridDim.x;
+  const unsigned g = b / group, g0 = g * group;
+  const unsigned in_group = G - g0 < group ? G - g0 : group;
+  const unsigned groups = (G + group - 1) / group;
+  if (!publish_with_ticket([&] { store_record(partials + uint64_t(b) * kRecordWords, block_total); },
+                           counters + 1 + g, in_group, &flag))
+    return;
+  const Exact gv = combine_records(partials + uint64_t(g0) * kRecordWords, in_group, lds);
+  if (groups == 1) {
+    if (threadIdx.x == 0) finish_exact(gv, out, out_fixed);
+    return;
+  }
+  __syncthreads();
+  if (!publish_with_ticket([&] { store_record(group_partials + uint64_t(g) * kRecordWords, gv); },
+                           counters, groups, &flag))
+    return;
+  const Exact v = combine_records(group_partials, groups, lds);
+  if (threadIdx.x == 0) finish_exact(v, out, out_fixed);
+}
+
+// n == 0: out = +0.0, the 128-bit sum 0.
+__global__ void exact_zero_kernel(float* out, int64_t* out_fixed) {
+  if (threadIdx.x == 0) {
+    out[0] = 0.0f;
+    if (out_fixed) {
+      out_fixed[0] = 0;
+      out_fixed[1] = 0;
+    }
+  }
+}
+
+template <int R>
+const void* pick_exact(bool nt) {
+  return nt ? reinterpret_cast<const void*>(&exact_kernel<R, true>)
+            : reinterpret_cast<const void*>(&exact_kernel<R, false>);
+}
+
+const void* exact_kernel_for(int r, bool nt) {
+  switch (r) {
+    case 1: return pick_exact<1>(nt);
+    case 2: return pick_exact<2>(nt);
+    case 3: return pick_exact<3>(nt);
+    case 4: return pick_exact<4>(nt);
+    case 5: return pick_exact<5>(nt);
+    case 6: return pick_exact<6>(nt);
+    case 7: return pick_exact<7>(nt);
+    case 8: return pick_exact<8>(nt);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_exact(const Plan& plan, const void* x, float* out, int64_t* out_fixed,
+                        void* ws, hipStream_t stream) {
+  if (plan.n == 0) {
+    void* args[] = {&out, &out_fixed};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&exact_zero_kernel), dim3(1), dim3(64),
+                           args, 0, stream);
+  }
+  const void* fn = exact_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  if (!fn) return hipErrorInvalidValue;
+  const u32x4* xv = static_cast<const u32x4*>(x);
+  uint64_t n = plan.n;
+  uint64_t chains_full = n / (uint64_t(plan.r) * kChunk);
+  char* base = static_cast<char*>(ws);
+  unsigned* counters = reinterpret_cast<unsigned*>(base);
+  uint64_t* partials = reinterpret_cast<uint64_t*>(base + kCounterBytes);
+  uint64_t* group_partials = reinterpret_cast<uint64_t*>(base + kCounterBytes + plan.partials_bytes);
+  unsigned group = plan.group;
+  void* args[] = {&xv, &n, &chains_full, &counters, &partials, &group_partials, &group, &out,
+                  &out_fixed};
+  return launch_main(plan, fn, args, stream);
+}
+
+}  // namespace armx

@@ -27,21 +27,37 @@ inline Workspace workspace_layout(const Plan& plan, void* ws) {
   return w;
 }
 
-// Launches the main kernel of a plan.  When the plan carries events they are
-// stamped by the kernel's own dispatch (start and completion) through
-// hipExtLaunchKernel; otherwise it is a plain hipLaunchKernel, which stream
-// capture (HIP graphs) records as an ordinary kernel node.
+// Launches a kernel.  Events, when given, are stamped by the kernel's own
+// dispatch (start and completion) through hipExtLaunchKernel; without them it
+// is a plain hipLaunchKernel, which stream capture (HIP graphs) records as an
+// ordinary kernel node.
+inline hipError_t launch_kernel(const void* fn, dim3 grid, dim3 block, void** args, size_t lds,
+                                hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (!start && !stop) return hipLaunchKernel(fn, grid, block, args, lds, stream);
+  return hipExtLaunchKernel(fn, grid, block, args, lds, stream, start, stop, 0);
+}
+
+// Launches the main kernel of a plan, stamping the plan's events if any.
 inline hipError_t launch_main(const Plan& plan, const void* fn, void** args, hipStream_t stream) {
-  const dim3 grid(unsigned(plan.grid)), block(unsigned(plan.waves * 64));
-  if (!plan.start_event && !plan.stop_event)
-    return hipLaunchKernel(fn, grid, block, args, plan.lds_bytes, stream);
-  return hipExtLaunchKernel(fn, grid, block, args, plan.lds_bytes, stream,
-                            static_cast<hipEvent_t>(plan.start_event),
-                            static_cast<hipEvent_t>(plan.stop_event), 0);
+  return launch_kernel(fn, dim3(unsigned(plan.grid)), dim3(unsigned(plan.waves * 64)), args,
+                       plan.lds_bytes, stream, static_cast<hipEvent_t>(plan.start_event),
+                       static_cast<hipEvent_t>(plan.stop_event));
 }
 
 // out[0] = sum of x[0..plan.n); ws holds the counter and the block results.
 hipError_t launch_sum(const Plan& plan, const void* x, float* out, void* ws, hipStream_t stream);
+
+// out[0] = sum of x[0..plan.n) by levels of MMA-only chain reductions, one
+// launch per level; ws holds the level buffers after its counter region.
+// The plan's start event is stamped by the first launch, its stop event by
+// the last.
+hipError_t launch_levels(const Plan& plan, const void* x, float* out, void* ws,
+                         hipStream_t stream);
+
+// out[0] = the binary32 nearest to the exact sum of x[0..plan.n); out_fixed
+// (may be null) = that sum as a 128-bit count of 2^-24 (low word, high word).
+hipError_t launch_exact(const Plan& plan, const void* x, float* out, int64_t* out_fixed,
+                        void* ws, hipStream_t stream);
 
 // out[0] = balanced-tree sum of x[0..plan.n).
 hipError_t launch_fixed(const Plan& plan, const void* x, float* out, void* ws,

@@ -5,7 +5,8 @@ namespace armx {
 namespace {
 
 constexpr unsigned kKnownFlags = ARMX_FLAG_PLAIN | ARMX_FLAG_CACHED_LOADS |
-                                 ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS;
+                                 ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS |
+                                 ARMX_FLAG_MMA_LEVELS;
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
@@ -36,7 +37,7 @@ uint64_t persistent_blocks(const OpDefaults& d, int cu_count, uint64_t W, uint64
 // groups.  Sets the workspace sizes.
 constexpr uint64_t kSingleLevelMax = 1024;
 
-void size_ticket(Plan& p) {
+void size_ticket(Plan& p, size_t record_bytes = sizeof(float)) {
   const uint64_t G = uint64_t(p.grid);
   uint64_t group = 1;
   if (G <= kSingleLevelMax) {
@@ -46,20 +47,22 @@ void size_ticket(Plan& p) {
     while ((G + group - 1) / group > kMaxGroups) group <<= 1;
   }
   p.group = unsigned(group);
-  p.partials_bytes = round_up(sizeof(float) * size_t(G), 256);
-  p.ws_bytes = kCounterBytes + p.partials_bytes + 256;
+  p.partials_bytes = round_up(record_bytes * size_t(G), 256);
+  p.ws_bytes = kCounterBytes + p.partials_bytes + round_up(record_bytes * kMaxGroups, 256);
 }
 
 }  // namespace
 
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
               const armx_config* cfg, int cu_count, Plan* plan) {
-  const OpDefaults d = op == kOpFixed       ? kFixedDefaults
-                       : op == kOpRows      ? kRowsDefaults
-                       : op == kOpRowsFixed ? kRowsFixedDefaults
-                                            : kSumDefaults;
   armx_config c{};
   if (cfg) c = *cfg;
+  const OpDefaults d = op == kOpFixed                    ? kFixedDefaults
+                       : op == kOpRows                   ? kRowsDefaults
+                       : op == kOpRowsFixed              ? kRowsFixedDefaults
+                       : op == kOpExact                  ? kExactDefaults
+                       : (c.flags & ARMX_FLAG_MMA_LEVELS) ? kLevelsDefaults
+                                                         : kSumDefaults;
   if (c.block_threads == 0) c.block_threads = d.block;
   if (c.chain_r == 0) c.chain_r = d.r;
   if (c.block_threads < 64 || c.block_threads > 64 * kMaxWaves || c.block_threads % 64)
@@ -78,8 +81,26 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   p.stop_event = c.stop_event;
   const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
 
-  if (op == kOpSum) {
+  if (op != kOpSum && (c.flags & ARMX_FLAG_MMA_LEVELS)) return ARMX_ERR_CONFIG;
+  if (op == kOpExact) {
+    // persistent grid as for the free-order sum; only the load kind is a flag
+    if (c.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS)) return ARMX_ERR_CONFIG;
     const uint64_t n = n_or_rows;
+    if (n > kMaxN) return ARMX_ERR_SHAPE;
+    p.n = n;
+    if (n == 0) { *plan = p; return ARMX_OK; }
+    const uint64_t chains = ceil_div(n, kChunk * R);
+    uint64_t grid = ceil_div(chains, W);
+    const uint64_t resident = persistent_blocks(d, cu_count, W, R);
+    if (grid > resident) grid = resident;
+    if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) grid = uint64_t(c.grid_blocks);
+    if (grid < 1) grid = 1;
+    p.grid = int(grid);
+    size_ticket(p, kExactRecordBytes);
+  } else if (op == kOpSum) {
+    const uint64_t n = n_or_rows;
+    if ((c.flags & ARMX_FLAG_MMA_LEVELS) && (c.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_TWO_PASS)))
+      return ARMX_ERR_CONFIG;
     if (n > kMaxN) return ARMX_ERR_SHAPE;
     p.n = n;
     if (n == 0) { *plan = p; return ARMX_OK; }
@@ -96,7 +117,19 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     if (grid < 1) grid = 1;
     if (grid > 0x7FFFFFFFull) return ARMX_ERR_SHAPE;
     p.grid = int(grid);
-    size_ticket(p);
+    if (c.flags & ARMX_FLAG_MMA_LEVELS) {
+      // level buffers: level 1's values, then level 2's (levels 3, 4, ...
+      // reuse them in turn); nothing when level 1 already gives one value
+      const uint64_t c1 = level_count(n, R, 1);
+      const uint64_t c2 = level_count(c1, R, 2);
+      if (c1 > 1) {
+        p.partials_bytes = round_up(sizeof(float) * size_t(c1), 256);
+        p.aux_bytes = c2 > 1 ? round_up(sizeof(float) * size_t(c2), 256) : 0;
+        p.ws_bytes = kCounterBytes + p.partials_bytes + p.aux_bytes;
+      }
+    } else {
+      size_ticket(p);
+    }
   } else if (op == kOpFixed) {
     const uint64_t n = n_or_rows;
     if (n > kMaxN) return ARMX_ERR_SHAPE;

@@ -32,6 +32,13 @@ constexpr OpDefaults kSumDefaults{128, 8, 16};
 constexpr OpDefaults kFixedDefaults{128, 8, 16};
 constexpr OpDefaults kRowsDefaults{64, 8, 16};
 constexpr OpDefaults kRowsFixedDefaults{64, 8, 16};
+// The MMA-levels form: its level-1 chains end in a longer dependent MFMA
+// sequence, and measured on MI355X more wavefronts per compute unit (about 8
+// at R = 8) hide it best.
+constexpr OpDefaults kLevelsDefaults{256, 8, 64};
+constexpr OpDefaults kExactDefaults{128, 8, 16};
+// Exact sum: each block publishes a 32-byte record (two 64-bit limbs, flags).
+constexpr size_t kExactRecordBytes = 32;
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;
 // Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.
@@ -48,7 +55,8 @@ enum Op {
   kOpSum = ARMX_OP_SUM,
   kOpRows = ARMX_OP_ROWS,
   kOpFixed = ARMX_OP_FIXED,
-  kOpRowsFixed = ARMX_OP_ROWS_FIXED
+  kOpRowsFixed = ARMX_OP_ROWS_FIXED,
+  kOpExact = ARMX_OP_EXACT
 };
 
 struct Plan {
@@ -66,11 +74,21 @@ struct Plan {
   uint64_t rows = 0;
   uint64_t ld = 0;
   size_t ws_bytes = 0;      // workspace the launch needs
-  size_t partials_bytes = 0;  // block-result region of the workspace
+  size_t partials_bytes = 0;  // block-result region of the workspace (MMA levels:
+                              // the first level buffer)
+  size_t aux_bytes = 0;       // MMA levels: the second level buffer
   unsigned group = 1;       // blocks per completion group (a power of two)
   void* start_event = nullptr;  // hipEvent_t stamped around the main kernel
   void* stop_event = nullptr;
 };
+
+// MMA levels (ARMX_FLAG_MMA_LEVELS): the number of fp32 values level `level`
+// produces from `count` inputs -- one per chain of R x 512 binary16 values at
+// level 1, one per chain of R x 256 fp32 values above.
+inline uint64_t level_count(uint64_t count, uint64_t r, int level) {
+  const uint64_t per_chain = r * (level == 1 ? kChunk : 256);
+  return (count + per_chain - 1) / per_chain;
+}
 
 // Resolves and checks a configuration for `op`.  `cu_count` is the number of
 // compute units of the target device.  Returns ARMX_OK or a negative status;

@@ -16,8 +16,14 @@ other rows of the hot path (MFMA-free design, fixed balanced-tree order, row
 sums, fixed-order row sums, one-chain-per-wavefront grids) on their own
 workloads.
 
+`--levels-sweep` times the recursive all-MMA form (one launch per level)
+against the single-launch form over n = 2^9 .. 2^28, for the running-time
+model T(n) = 5 log_{m^2}(n) of "GPU Tensor Cores for fast Arithmetic
+Reductions" (arXiv 2001.05585, Abstract), which counts levels.
+
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
-                    [--no-cpu-baseline] [--sweep] [--copy-calibration]
+                    [--no-cpu-baseline] [--sweep] [--levels-sweep]
+                    [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -77,6 +83,15 @@ def event_timed(torch, fn, iters: int, warmup: int = 5):
     return sum(times) / len(times), times[len(times) // 2]
 
 
+def mma_levels_count(n: int, r: int) -> int:
+    """Launches of the MMA-levels form: one value per R x 512 inputs at level
+    1, per R x 256 values above, until one value is left."""
+    c, k = -(-n // (512 * r)), 1
+    while c > 1:
+        c, k = -(-c // (256 * r)), k + 1
+    return k
+
+
 def cpu_baseline(x_np, budget_s: float = 12.0):
     """The exact-sum oracle on the host: whole passes over the input until
     `budget_s` of CPU time is spent (at least one pass).  Returns the record
@@ -107,6 +122,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the block x R matrix (paper-faithful and persistent grids)")
+    ap.add_argument("--levels-sweep", action="store_true",
+                    help="also time the MMA-levels form against the single-launch form "
+                         "over n = 2^lo .. 2^hi (level count vs time)")
+    ap.add_argument("--levels-log2", default="9-28",
+                    help="lo-hi: the sizes of --levels-sweep (default 9-28)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch) five times, the "
                          "known-size reference for HBM byte counters")
@@ -212,6 +232,12 @@ def main() -> int:
         var["one_chain_b256_r4_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
         ms, med = event_timed(torch, lambda i: bufs[i & 1].sum(dtype=torch.float32), 100)
         var["torch_sum_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
+        for r in (8, 4):
+            ms, med = event_timed(torch, lambda i: armx.reduce_sum(
+                bufs[i & 1], mma_levels=True, chain_r=r), 200)
+            var[f"mma_levels_r{r}_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6,
+                                            "launches": mma_levels_count(n, r),
+                                            "vs_single_launch": avg_ms / ms}
 
         xf_np = si.workload("fixed_2p26_u11")
         fbufs = [torch.from_numpy(xf_np).to(dev)]
@@ -259,6 +285,58 @@ def main() -> int:
                     print(key, f"{ms * 1e3:.1f} us", f"{2 * n / ms / 1e6:.0f} GB/s",
                           file=sys.stderr, flush=True)
         record["sweep"] = sweep
+
+    if args.levels_sweep:
+        # GPU time per call with the queue kept full: a sleep kernel holds the
+        # GPU while the host enqueues the whole batch, so the calls then run
+        # back to back and the host's submission rate does not enter.  Inputs
+        # are prefixes of the headline buffer (contiguous, aligned); rotation
+        # only matters once a prefix outgrows the Infinity Cache.
+        probe_s, probe_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        probe_s.record()
+        torch.cuda._sleep(1 << 22)
+        probe_e.record()
+        torch.cuda.synchronize()
+        cycles_per_ms = (1 << 22) / probe_s.elapsed_time(probe_e)
+
+        def queued_us(fn, calls):
+            fn(0)
+            torch.cuda.synchronize()
+            s_ev, e_ev = (torch.cuda.Event(enable_timing=True),
+                          torch.cuda.Event(enable_timing=True))
+            torch.cuda._sleep(int(cycles_per_ms * max(4.0, calls * 0.05)))
+            s_ev.record()
+            h0 = time.perf_counter()
+            for i in range(calls):
+                fn(i)
+            host_ms = (time.perf_counter() - h0) * 1e3
+            e_ev.record()
+            torch.cuda.synchronize()
+            gpu_ms = s_ev.elapsed_time(e_ev)
+            return gpu_ms * 1e3 / calls, host_ms < max(4.0, calls * 0.05)
+
+        lv = {}
+        lo, hi = (int(v) for v in args.levels_log2.split("-"))
+        if not 0 <= lo <= hi <= 28:
+            print("--levels-log2 must lie within 0-28", file=sys.stderr)
+            return 2
+        for k in range(lo, hi + 1):
+            m = 1 << k
+            views = [bufs[0][:m], bufs[1][:m]]
+            calls = 100 if k < 26 else 40
+            row = {"n": m}
+            for r in (1, 8):      # block size: the levels form's default
+                us, ok = queued_us(lambda i: armx.reduce_sum(
+                    views[i & 1], out=out, mma_levels=True, chain_r=r), calls)
+                row[f"launches_r{r}"] = mma_levels_count(m, r)
+                row[f"mma_levels_r{r}_us"] = us
+                row[f"queue_full_r{r}"] = ok
+            us, ok = queued_us(lambda i: armx.reduce_sum(views[i & 1], out=out), calls)
+            row["single_launch_us"] = us
+            row["queue_full_single"] = ok
+            lv[f"2^{k}"] = row
+            print(f"n=2^{k}", json.dumps(row), file=sys.stderr, flush=True)
+        record["levels_sweep"] = lv
 
     if not args.no_cpu_baseline:
         record["cpu_baseline"], e = cpu_baseline(x_np)

@@ -44,6 +44,7 @@
 #define ARMX_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -75,6 +76,9 @@ typedef enum armx_status {
 #define ARMX_FLAG_TWO_PASS 0x8u    /* reduce_sum / fixed order: a second launch */
                                    /* combines the block results instead of    */
                                    /* the last block to finish                 */
+#define ARMX_FLAG_MMA_LEVELS 0x10u /* reduce_sum: the recursive all-MMA form   */
+                                   /* (see reduce_sum); not with PLAIN or      */
+                                   /* TWO_PASS                                 */
 
 typedef struct armx_config {
   int block_threads; /* 0 = default; else 64..1024, a multiple of 64.         */
@@ -91,10 +95,12 @@ typedef struct armx_config {
 } armx_config;
 /* Defaults (block_threads, chain_r), measured on MI355X:
  *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8;
- *   reduce_rows_fixed_order 64, 8.
+ *   reduce_rows_fixed_order 64, 8; reduce_sum with ARMX_FLAG_MMA_LEVELS
+ *   256, 8; reduce_sum_exact 128, 8.
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
- * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth),
- * and at least one block per compute unit. */
+ * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth;
+ * 64 / R for the MMA-levels form), and at least one block per compute
+ * unit. */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.
@@ -116,6 +122,18 @@ typedef struct armx_config {
  * them into fp32 accumulators.  The order of additions depends on the
  * configuration (not on timing): two calls with the same n, configuration
  * and device give the same bits.
+ *
+ * With ARMX_FLAG_MMA_LEVELS the sum is computed in the recursive form whose
+ * level count the same Abstract's running-time model T(n) = 5 log_{m^2}(n)
+ * counts: level 1 reduces every chain of R x 512 values to one fp32 with
+ * MFMAs only (the tiles as the A operand against ones give 16 row sums; four
+ * v_mfma_f32_16x16x4_f32 against ones add those), and each further level
+ * reduces chains of R x 256 fp32 values of the level below the same way,
+ * one launch per level, until one value is left.  Its result depends on n
+ * and R only (not on block size or grid).  The workspace holds the level
+ * buffers: about 4 * ceil(n / (512 R)) bytes plus the counter region (0
+ * bytes when n <= 512 R); the counter region is left untouched.  start_event
+ * is stamped by the first level's launch and stop_event by the last.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  */
 int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
@@ -187,18 +205,50 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
 int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
                             void* ws, size_t ws_bytes, const armx_config* cfg, void* stream);
 
+/*
+ * reduce_sum_exact -- out[0] = the binary32 nearest (ties to even) to the
+ * exact real sum of x[0..n); the same bits for every configuration.
+ *
+ *   The operation of "GPU Tensor Cores for fast Arithmetic Reductions",
+ *   Abstract, without rounding error until the final 32-bit result: every
+ *   binary16 value is an integer count of 2^-24, so the sum is kept as an
+ *   integer split into two limbs with weights 1 and 2^32 -- components with
+ *   fixed weights recombined exactly, as in "AWE: Adaptive Weight Encoding
+ *   for Exact Integer Matrix Products with Fewer GEMMs on FP4 Tensor Cores"
+ *   (arXiv 2609.24519), Abstract.  Integer addition is associative, so the
+ *   result cannot depend on block size, chain length, grid or device, and it
+ *   equals the correctly rounded sum.
+ *
+ * x, n, ws, ws_bytes, stream as for reduce_sum (the workspace holds 32 bytes
+ * per block after its counter region).
+ * out        device, 1 binary32.  n == 0, or an exact sum of zero, gives +0.0.
+ * out_fixed  device, 2 int64 words, 8-byte aligned, or NULL: the exact sum
+ *            as a 128-bit two's complement count of 2^-24 (out_fixed[0] the
+ *            low 64 bits, out_fixed[1] the high 64 bits, signed); 0 when an
+ *            input is an infinity or a NaN.
+ * cfg        host, may be NULL.  Only ARMX_FLAG_CACHED_LOADS is accepted.
+ * Each lane adds a chain's 8 R values in binary64 (exact: every partial sum
+ * is a multiple of 2^-24 below 2^22), and the chain totals accumulate as
+ * integers; no MFMA is used.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
+ */
+int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, void* ws,
+                     size_t ws_bytes, const armx_config* cfg, void* stream);
+
 /* Operation codes for armx_workspace_bytes. */
 #define ARMX_OP_SUM 0
 #define ARMX_OP_ROWS 1
 #define ARMX_OP_FIXED 2
 #define ARMX_OP_ROWS_FIXED 3
+#define ARMX_OP_EXACT 4
 
 /*
  * armx_workspace_bytes -- bytes of workspace the matching call needs on the
  * current device with this configuration (0 if none).  `n_or_rows` is n for
- * ARMX_OP_SUM / ARMX_OP_FIXED and rows for ARMX_OP_ROWS; `cols` is used by
- * ARMX_OP_ROWS only.  Returns (size_t)-1 for an invalid op or configuration.
- * Needs no GPU: without a device it assumes 256 compute units.
+ * ARMX_OP_SUM / ARMX_OP_FIXED / ARMX_OP_EXACT and rows for ARMX_OP_ROWS and
+ * ARMX_OP_ROWS_FIXED; `cols` is used by those two only.  Returns (size_t)-1
+ * for an invalid op or configuration.  Needs no GPU: without a device it
+ * assumes 256 compute units.
  */
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
                             const armx_config* cfg);
@@ -206,7 +256,7 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 3. */
+/* armx_version -- ABI version of this header: 5. */
 int armx_version(void);
 
 #ifdef __cplusplus

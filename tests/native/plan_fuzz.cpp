@@ -39,7 +39,7 @@ int main(int argc, char** argv) {
   };
   int accepted = 0;
   for (int it = 0; it < iters; ++it) {
-    const int op = int(rng() % 5);  // 4 is not an operation
+    const int op = int(rng() % 6);  // 5 is not an operation
     armx_config c{};
     c.block_threads = (rng() % 4 == 0) ? 0 : int(rng() % 1200);
     if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
@@ -52,8 +52,8 @@ int main(int argc, char** argv) {
     const int cus = int(1 + rng() % 512);
     Plan p;
     const int st = armx::make_plan(op, n, cols, ld, &c, cus, &p);
-    if (op == 4) {
-      EXPECT(st == ARMX_ERR_CONFIG, "op 4 accepted");
+    if (op == 5) {
+      EXPECT(st == ARMX_ERR_CONFIG, "op 5 accepted");
       continue;
     }
     EXPECT(st <= 0 && st >= ARMX_ERR_HIP, "status %d", st);
@@ -62,6 +62,38 @@ int main(int argc, char** argv) {
     const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
     EXPECT(W >= 1 && W <= 16 && R >= 1 && R <= 8, "W %llu R %llu", (unsigned long long)W,
            (unsigned long long)R);
+    const bool levels = (p.flags & ARMX_FLAG_MMA_LEVELS) != 0;
+    EXPECT(!levels || op == ARMX_OP_SUM, "levels flag accepted for op %d", op);
+    if (levels) {
+      EXPECT(!(p.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_TWO_PASS)), "levels flags");
+      if (p.n == 0) continue;
+      const uint64_t c1 = armx::level_count(p.n, R, 1), c2 = armx::level_count(c1, R, 2);
+      if (c1 == 1) {
+        EXPECT(p.ws_bytes == 0, "levels ws for one level");
+      } else {
+        EXPECT(p.partials_bytes >= 4 * c1 && p.partials_bytes % 256 == 0, "level-1 buffer");
+        EXPECT(c2 == 1 ? p.aux_bytes == 0 : (p.aux_bytes >= 4 * c2 && p.aux_bytes % 256 == 0),
+               "level-2 buffer");
+        EXPECT(p.ws_bytes == armx::kCounterBytes + p.partials_bytes + p.aux_bytes, "levels ws");
+      }
+      // every level's chain count fits the level-k grid
+      for (uint64_t c = c1; c > 1;) {
+        c = armx::level_count(c, R, 2);
+        EXPECT(cdiv(c, W) <= 0x7FFFFFFFull, "level grid");
+      }
+      continue;
+    }
+    if (op == ARMX_OP_EXACT) {
+      EXPECT(!(p.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS)), "exact flags");
+      if (p.n == 0) continue;
+      EXPECT(p.grid >= 1 && uint64_t(p.grid) <= cdiv(cdiv(p.n, 512 * R), W), "exact grid");
+      EXPECT(pow2(p.group) && cdiv(uint64_t(p.grid), p.group) <= armx::kMaxGroups, "groups");
+      EXPECT(p.partials_bytes >= armx::kExactRecordBytes * uint64_t(p.grid) &&
+             p.partials_bytes % 256 == 0, "exact records");
+      EXPECT(p.ws_bytes >= armx::kCounterBytes + p.partials_bytes +
+                              armx::kExactRecordBytes * armx::kMaxGroups, "exact ws");
+      continue;
+    }
     if (op == ARMX_OP_SUM || op == ARMX_OP_FIXED) {
       if (p.n == 0) continue;
       EXPECT(p.grid >= 1, "grid %d", p.grid);

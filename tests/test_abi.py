@@ -21,7 +21,7 @@ def _declared_functions():
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
     for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
-              "armx_workspace_bytes", "armx_status_string", "armx_version"):
+              "reduce_sum_exact", "armx_workspace_bytes", "armx_status_string", "armx_version"):
         assert f in names
 
 
@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 3
+    assert armx.lib.armx_version() == 5
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
@@ -71,6 +71,73 @@ def test_fixed_order_config_rules():
     assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(block_threads=192), None) == -3   # not 2^k
     assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(plain=True), None) == -3
     assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(one_chain=True), None) == -3
+
+
+def test_exact_argument_errors():
+    f = armx.lib.reduce_sum_exact
+    ws = 1 << 24
+    assert f(None, 10, FAKE, None, ws, 1 << 20, None, None) == -1          # x NULL
+    assert f(FAKE, 10, None, None, ws, 1 << 20, None, None) == -1          # out NULL
+    assert f(FAKE + 2, 10, FAKE, None, ws, 1 << 20, None, None) == -2      # x misaligned
+    assert f(FAKE, 10, FAKE, FAKE + 4, ws, 1 << 20, None, None) == -2      # out_fixed
+    for bad in (dict(plain=True), dict(one_chain=True), dict(two_pass=True),
+                dict(mma_levels=True), dict(chain_r=9), dict(block_threads=96)):
+        assert f(FAKE, 10, FAKE, None, ws, 1 << 20, cfg(**bad), None) == -3, bad
+    assert f(FAKE, 10, FAKE, None, None, 0, None, None) == -1              # ws needed
+    assert f(FAKE, 10, FAKE, None, ws, 8, None, None) == -4                # ws too small
+    assert f(FAKE, (1 << 40) + 1, FAKE, None, ws, 1 << 30, None, None) == -5
+
+
+def test_exact_workspace_sizes():
+    # counter region + 32-byte records per block + 63 group records
+    def ws(grid):
+        return 256 + (32 * grid + 255) // 256 * 256 + 2048
+    assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28) == ws(256)
+    assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28, block_threads=64) == ws(512)
+    assert armx.workspace_bytes(armx.OP_EXACT, 1000) == ws(1)
+    assert armx.workspace_bytes(armx.OP_EXACT, 0) == 0
+    assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28, grid_blocks=3000) == ws(256)
+    assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28, chain_r=1, block_threads=64,
+                                grid_blocks=3000) == ws(3000)
+
+
+def test_fixed_to_int():
+    import torch
+    for v in (0, 1, -1, 2 ** 63, -(2 ** 63), 2 ** 80 + 12345, -(2 ** 80) - 7):
+        lo = v & ((1 << 64) - 1)
+        lo = lo - (1 << 64) if lo >= 1 << 63 else lo
+        hi = v >> 64
+        assert armx.fixed_to_int(torch.tensor([lo, hi], dtype=torch.int64)) == v
+
+
+def test_mma_levels_config_rules():
+    f = armx.lib.reduce_sum
+    ws = 1 << 24
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(mma_levels=True, plain=True), None) == -3
+    assert f(FAKE, 10, FAKE, ws, 1 << 20, cfg(mma_levels=True, two_pass=True), None) == -3
+    assert armx.lib.reduce_sum_fixed_order(FAKE, 10, FAKE, ws, 1 << 20,
+                                           cfg(mma_levels=True), None) == -3
+    assert armx.lib.reduce_rows(FAKE, 4, 96, 96, FAKE, None, 0, cfg(mma_levels=True), None) == -3
+    # a second level needs the level buffers
+    assert f(FAKE, 1 << 20, FAKE, None, 0, cfg(mma_levels=True), None) == -1
+    assert f(FAKE, 1 << 20, FAKE, ws, 256, cfg(mma_levels=True), None) == -4
+
+
+def test_mma_levels_workspace_sizes():
+    # counter region + level-1 values + level-2 values, each rounded to 256 B;
+    # nothing when level 1 gives one value (n <= 512 R)
+    def r256(v):
+        return (v + 255) // 256 * 256
+    for n, r in ((1 << 28, 8), (1 << 28, 1), ((1 << 20) + 1, 4), (3000, 1)):
+        c1 = -(-n // (512 * r))
+        c2 = -(-c1 // (256 * r))
+        want = 256 + r256(4 * c1) + (r256(4 * c2) if c2 > 1 else 0)
+        assert armx.workspace_bytes(armx.OP_SUM, n, chain_r=r, mma_levels=True) == want, (n, r)
+    assert armx.workspace_bytes(armx.OP_SUM, 4096, chain_r=8, mma_levels=True) == 0
+    assert armx.workspace_bytes(armx.OP_SUM, 4097, chain_r=8, mma_levels=True) == 256 + 256
+    # the grid does not change the level buffers
+    assert (armx.workspace_bytes(armx.OP_SUM, 1 << 24, mma_levels=True, block_threads=1024)
+            == armx.workspace_bytes(armx.OP_SUM, 1 << 24, mma_levels=True, one_chain=True))
 
 
 def test_rows_argument_errors():
