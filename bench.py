@@ -12,9 +12,9 @@ one launch (2 bytes per element) divided by the average kernel time, measured
 with HIP events that the kernel's own dispatch stamps (hipExtLaunchKernel) on
 the stream it runs on, on every 8th step of the timed region.  `cpu_baseline` is
 the CPU oracle (exact integer sum) timed on this host.  `variants` times the
-other rows of the hot path (MFMA-free design, fixed balanced-tree order, row
-sums, fixed-order row sums, one-chain-per-wavefront grids) on their own
-workloads.
+other rows of the hot path (MFMA-free design, exact sum, MMA-levels form,
+fixed balanced-tree order, row sums, fixed-order row sums,
+one-chain-per-wavefront grids) on their own workloads.
 
 `--levels-sweep` times the recursive all-MMA form (one launch per level)
 against the single-launch form over n = 2^9 .. 2^28, for the running-time
@@ -232,6 +232,10 @@ def main() -> int:
         var["one_chain_b256_r4_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
         ms, med = event_timed(torch, lambda i: bufs[i & 1].sum(dtype=torch.float32), 100)
         var["torch_sum_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1]), 200)
+        exact_val = armx.reduce_sum_exact(bufs[0]).cpu().numpy()
+        var["exact_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "vs_free_order": avg_ms / ms,
+                             "result_bits": int(exact_val.view(np.uint32))}
         for r in (8, 4):
             ms, med = event_timed(torch, lambda i: armx.reduce_sum(
                 bufs[i & 1], mma_levels=True, chain_r=r), 200)
@@ -342,6 +346,10 @@ def main() -> int:
         record["cpu_baseline"], e = cpu_baseline(x_np)
         record["check"] = {"exact_sum": e.f64, "abs_err": abs(result - e.f64),
                            "rel_err": abs(result - e.f64) / abs(e.f64)}
+        if "variants" in record:
+            want = int(np.float32(e.f32).view(np.uint32))
+            record["check"]["exact_variant_matches_oracle"] = (
+                record["variants"]["exact_2p28"]["result_bits"] == want)
 
     print(json.dumps(record), flush=True)
     return 0
