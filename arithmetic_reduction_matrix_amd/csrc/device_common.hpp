@@ -241,6 +241,14 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
                                               uint64_t iters, uint64_t stride, int lane,
                                               float& run) {
   if (iters == 0) return;
+  if (iters == 1) {
+    // a single chain (the one-chain-per-wavefront grid): no prefetch, so the
+    // chain is not loaded again while its first load is still in flight
+    u32x4 v[R];
+    load_chain<R, NT>(base, c0, lane, v);
+    run += chain_value<R, PLAIN>(v);
+    return;
+  }
   const uint64_t last = c0 + (iters - 1) * stride;
   u32x4 a[R], b[R];
   float pending = 0.0f;

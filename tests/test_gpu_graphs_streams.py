@@ -37,12 +37,20 @@ def test_graph_capture_and_replay():
     o_rfix = torch.empty(256, dtype=torch.float32, device="cuda")
     ws_sum = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device="cuda")
     ws_fix = torch.zeros(armx.workspace_bytes(armx.OP_FIXED, n), dtype=torch.uint8, device="cuda")
+    o_ex = torch.empty((), dtype=torch.float32, device="cuda")
+    o_exq = torch.zeros(2, dtype=torch.int64, device="cuda")
+    ws_ex = torch.zeros(armx.workspace_bytes(armx.OP_EXACT, n), dtype=torch.uint8, device="cuda")
+    o_lv = torch.empty((), dtype=torch.float32, device="cuda")
+    ws_lv = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n, mma_levels=True), dtype=torch.uint8,
+                        device="cuda")
 
     def calls():
         armx.reduce_sum(x, out=o_sum, workspace=ws_sum)
         armx.reduce_sum_fixed_order(x, out=o_fix, workspace=ws_fix)
         armx.reduce_rows(m, out=o_rows)
         armx.reduce_rows_fixed_order(m, out=o_rfix)
+        armx.reduce_sum_exact(x, out=o_ex, fixed=o_exq, workspace=ws_ex)
+        armx.reduce_sum(x, out=o_lv, workspace=ws_lv, mma_levels=True)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -61,21 +69,30 @@ def test_graph_capture_and_replay():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = [_bits(o_sum), _bits(o_fix), _bits(o_rows), _bits(o_rfix)]
+        got = [_bits(o_sum), _bits(o_fix), _bits(o_rows), _bits(o_rfix), _bits(o_ex),
+               _bits(o_lv)]
+        got_q = armx.fixed_to_int(o_exq.cpu())
         # eager calls on the same data (own outputs and workspaces)
         e_sum = armx.reduce_sum(x)
         e_fix = armx.reduce_sum_fixed_order(x)
         e_rows = armx.reduce_rows(m)
         e_rfix = armx.reduce_rows_fixed_order(m)
+        e_ex = armx.reduce_sum_exact(x)
+        e_lv = armx.reduce_sum(x, mma_levels=True)
         torch.cuda.synchronize()
         assert np.array_equal(got[0], _bits(e_sum)), rep
         assert np.array_equal(got[1], _bits(e_fix)), rep
         assert np.array_equal(got[2], _bits(e_rows)), rep
         assert np.array_equal(got[3], _bits(e_rfix)), rep
+        assert np.array_equal(got[4], _bits(e_ex)), rep
+        assert np.array_equal(got[5], _bits(e_lv)), rep
         if rep in (0, 4):
             xh = pool[rep].cpu().numpy()
+            e = exact_sum(xh)
             assert got[1][()] == bits32(fixed_tree_sum(xh))
-            check_free_order(float(o_sum.item()), exact_sum(xh), f"replay {rep}")
+            assert got[4][()] == bits32(e.f32) and got_q == e.q
+            check_free_order(float(o_sum.item()), e, f"replay {rep}")
+            check_free_order(float(o_lv.item()), e, f"levels replay {rep}")
 
 
 def test_concurrent_streams():
