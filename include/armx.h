@@ -95,7 +95,7 @@ typedef struct armx_config {
 } armx_config;
 /* Defaults (block_threads, chain_r), measured on MI355X:
  *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8;
- *   reduce_rows_fixed_order 64, 8; reduce_sum with ARMX_FLAG_MMA_LEVELS
+ *   reduce_rows_fixed_order 64, 4; reduce_sum with ARMX_FLAG_MMA_LEVELS
  *   256, 8; reduce_sum_exact 128, 8.
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
  * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth;
@@ -199,7 +199,7 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  * rows > 1).  ws unused (may be NULL).  block_threads must be a power of
  * two.  ARMX_FLAG_PLAIN, ARMX_FLAG_ONE_CHAIN and ARMX_FLAG_TWO_PASS are not
  * accepted.  Rows longer than the LDS node logs allow (about 2^26 values at
- * R = 8, 2^23 at R = 1) return ARMX_ERR_SHAPE.
+ * R = 8, 2^25 at the default R = 4, 2^23 at R = 1) return ARMX_ERR_SHAPE.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
  */
 int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
