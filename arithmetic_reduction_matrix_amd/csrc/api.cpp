@@ -40,7 +40,7 @@ int check_ws(const armx::Plan& plan, const void* ws, size_t ws_bytes) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ARMX_OK : ARMX_ERR_HIP; }
 
-// Common checks of reduce_sum and reduce_sum_fixed_order.
+// Common checks of reduce_sum, reduce_sum_fixed_order and reduce_sum_exact.
 int prepare_flat(int op, const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
                  const armx_config* cfg, armx::Plan* plan) {
   if (!out) return ARMX_ERR_NULL;
@@ -94,8 +94,13 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, 
   if (rows > 0 && !out) return ARMX_ERR_NULL;
   if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
   if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  // configuration errors are reported before touching the device
+  armx::Plan probe;
+  int st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg, 256, &probe);
+  if (st != ARMX_OK) return st;
   armx::Plan plan;
-  int st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg, 256, &plan);
+  st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg,
+                       rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
   if (st != ARMX_OK) return st;
   return hip_status(armx::launch_rows(plan, x, out, static_cast<hipStream_t>(stream)));
 }
