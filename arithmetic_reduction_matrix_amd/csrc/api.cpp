@@ -4,6 +4,8 @@
 
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 
 #include "armx.h"
 #include "launch.h"
@@ -40,6 +42,23 @@ int check_ws(const armx::Plan& plan, const void* ws, size_t ws_bytes) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ARMX_OK : ARMX_ERR_HIP; }
 
+// With the environment variable ARMX_LOG set (to anything), every accepted
+// call writes its launch plan to stderr; otherwise the library never prints.
+bool log_enabled() {
+  static const bool on = std::getenv("ARMX_LOG") != nullptr;
+  return on;
+}
+
+void log_plan(const char* entry, const armx::Plan& p) {
+  if (!log_enabled()) return;
+  std::fprintf(stderr,
+               "armx: %s n=%llu rows=%llu ld=%llu grid=%d block=%d R=%d flags=0x%x "
+               "mode=%d lds=%zu ws=%zu group=%u\n",
+               entry, (unsigned long long)p.n, (unsigned long long)p.rows,
+               (unsigned long long)p.ld, p.grid, p.waves * 64, p.r, p.flags, p.mode, p.lds_bytes,
+               p.ws_bytes, p.group);
+}
+
 // Common checks of reduce_sum, reduce_sum_fixed_order and reduce_sum_exact.
 int prepare_flat(int op, const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
                  const armx_config* cfg, armx::Plan* plan) {
@@ -64,6 +83,7 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
   armx::Plan plan;
   int st = prepare_flat(armx::kOpSum, x, n, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
+  log_plan("reduce_sum", plan);
   if (plan.flags & ARMX_FLAG_MMA_LEVELS)
     return hip_status(armx::launch_levels(plan, x, out, ws, static_cast<hipStream_t>(stream)));
   return hip_status(armx::launch_sum(plan, x, out, ws, static_cast<hipStream_t>(stream)));
@@ -74,6 +94,7 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws, size_t
   armx::Plan plan;
   int st = prepare_flat(armx::kOpFixed, x, n, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
+  log_plan("reduce_sum_fixed_order", plan);
   return hip_status(armx::launch_fixed(plan, x, out, ws, static_cast<hipStream_t>(stream)));
 }
 
@@ -83,6 +104,7 @@ int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, vo
   int st = prepare_flat(armx::kOpExact, x, n, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
   if (out_fixed && !aligned(out_fixed, 8)) return ARMX_ERR_ALIGN;
+  log_plan("reduce_sum_exact", plan);
   return hip_status(
       armx::launch_exact(plan, x, out, out_fixed, ws, static_cast<hipStream_t>(stream)));
 }
@@ -102,6 +124,7 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, 
   st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg,
                        rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
   if (st != ARMX_OK) return st;
+  log_plan("reduce_rows", plan);
   return hip_status(armx::launch_rows(plan, x, out, static_cast<hipStream_t>(stream)));
 }
 
@@ -119,6 +142,7 @@ int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, 
   st = armx::make_plan(armx::kOpRowsFixed, rows, cols, ld, cfg,
                        rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
   if (st != ARMX_OK) return st;
+  log_plan("reduce_rows_fixed_order", plan);
   return hip_status(armx::launch_rows_fixed(plan, x, out, static_cast<hipStream_t>(stream)));
 }
 

@@ -214,6 +214,8 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "sum_kernel<R=8, non-temporal, MFMA>",
             "launch_ms_avg": avg_ms, "launch_ms_median": launch_ms[len(launch_ms) // 2],
+            "launch_ms_p10": launch_ms[len(launch_ms) // 10],
+            "launch_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
             "launches_timed": len(launch_ms),
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "kernel_source_sha256_16": kernel_source_hash(),

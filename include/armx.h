@@ -26,8 +26,11 @@
  *   no state between calls other than a per-device cache of the compute-unit
  *   count.
  * - Errors are returned as a negative armx_status before anything is
- *   enqueued; the library never prints and never aborts.  A failure reported
- *   by the HIP runtime while enqueueing returns ARMX_ERR_HIP.
+ *   enqueued; the library never aborts, and prints nothing unless the
+ *   environment variable ARMX_LOG is set, in which case every accepted call
+ *   writes one line with its launch plan (grid, block size, R, workspace) to
+ *   stderr.  A failure reported by the HIP runtime while enqueueing returns
+ *   ARMX_ERR_HIP.
  * - Workspace: `ws` points to at least armx_workspace_bytes(...) bytes,
  *   256-byte aligned.  Its first 256 bytes hold a completion counter that
  *   MUST be zero before the first call that uses the buffer; every call

@@ -1,0 +1,89 @@
+"""Out-of-bounds writes: every output and workspace region is placed between
+guard bands filled with a pattern; after each entry point runs (at sizes with
+ragged tails, several blocks and both ticket levels), the guards must be
+intact, the workspace's counter region must be back at zero, and the part of
+the workspace past what armx_workspace_bytes asks for must be untouched."""
+import pytest
+import torch
+
+import arithmetic_reduction_matrix_amd as armx
+import synth_inputs as si
+
+from _parity import require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096      # bytes on each side (a multiple of 256, so regions stay aligned)
+PATTERN = 0xA5
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class Guarded:
+    """`nbytes` usable bytes between two guard bands of PATTERN."""
+
+    def __init__(self, nbytes: int, fill: int = PATTERN):
+        self.n = nbytes
+        self.buf = torch.full((GUARD + nbytes + GUARD,), fill, dtype=torch.uint8, device="cuda")
+        self.buf[:GUARD] = PATTERN
+        self.buf[GUARD + nbytes:] = PATTERN
+
+    def body(self, dtype=torch.uint8):
+        return self.buf[GUARD:GUARD + self.n].view(dtype)
+
+    def guards_intact(self) -> bool:
+        g = torch.cat([self.buf[:GUARD], self.buf[GUARD + self.n:]])
+        return bool((g == PATTERN).all().item())
+
+
+SIZES = [1, 513, (1 << 20) + 37, (1 << 23) + 4097]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("name,op,cfg", [
+    ("sum", armx.OP_SUM, dict()),
+    ("sum-plain", armx.OP_SUM, dict(plain=True)),
+    ("sum-one-chain", armx.OP_SUM, dict(one_chain=True, block_threads=64, chain_r=1)),
+    ("sum-two-pass", armx.OP_SUM, dict(two_pass=True)),
+    ("sum-levels", armx.OP_SUM, dict(mma_levels=True, chain_r=1)),
+    ("fixed", armx.OP_FIXED, dict()),
+    ("exact", armx.OP_EXACT, dict()),
+])
+def test_flat_entry_points_stay_in_bounds(n, name, op, cfg):
+    x = to_dev(si.generate("uniform11", n, seed=n))
+    need = armx.workspace_bytes(op, n, **cfg)
+    spare = 1024
+    ws = Guarded(need + spare, fill=0)            # zero-filled workspace body
+    ws.body()[need:] = PATTERN                     # the unused tail keeps a pattern
+    out = Guarded(4)
+    fixed = Guarded(16)
+    kw = dict(out=out.body(torch.float32).reshape(()), **cfg)
+    if need:
+        kw["workspace"] = ws.body()[:need]
+    for _ in range(2):                             # the second call reuses the workspace
+        if op == armx.OP_EXACT:
+            armx.reduce_sum_exact(x, fixed=fixed.body(torch.int64), **kw)
+        elif op == armx.OP_FIXED:
+            armx.reduce_sum_fixed_order(x, **kw)
+        else:
+            armx.reduce_sum(x, **kw)
+    torch.cuda.synchronize()
+    assert out.guards_intact() and ws.guards_intact() and fixed.guards_intact(), (name, n)
+    assert bool((ws.body()[need:] == PATTERN).all().item()), (name, n, "workspace tail")
+    if need:   # the ticket paths restore their counters; the levels form never touches them
+        assert int(ws.body()[:256].count_nonzero().item()) == 0, (name, n, "counter region")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 700), (300, 4096), (4097, 2048 + 8)])
+@pytest.mark.parametrize("fixed_order", [False, True])
+def test_row_entry_points_stay_in_bounds(rows, cols, fixed_order):
+    ld = (cols + 7) // 8 * 8
+    m = to_dev(si.generate_rows("normal", rows, ld, seed=rows))[:, :cols]
+    out = Guarded(4 * rows)
+    fn = armx.reduce_rows_fixed_order if fixed_order else armx.reduce_rows
+    fn(m, out=out.body(torch.float32))
+    torch.cuda.synchronize()
+    assert out.guards_intact(), (rows, cols, fixed_order)
