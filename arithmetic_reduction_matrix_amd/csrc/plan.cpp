@@ -1,6 +1,8 @@
 // Argument checking and launch planning (host only, no HIP calls).
 #include "plan.h"
 
+#include <cmath>
+
 namespace armx {
 namespace {
 
@@ -27,6 +29,25 @@ uint64_t persistent_blocks(const OpDefaults& d, int cu_count, uint64_t W, uint64
   uint64_t blocks = uint64_t(cu_count) * waves_per_cu / W;
   if (blocks < uint64_t(cu_count)) blocks = uint64_t(cu_count);
   return blocks;
+}
+
+// Automatic grids for flat reductions of small inputs: a call costs about
+// a n / g (streaming per wavefront) + b g (block launch and completion ticket)
+// for g wavefronts, smallest near g ~ sqrt(n).  A wavefront streams R loads
+// per step, so the cap is sqrt(n) / R wavefronts; measured on MI355X at R = 8
+// (64 blocks of 2 at n = 2^20) it is within a few percent of the best grid
+// from 2^18 to 2^24 for the free-order, fixed-order and exact sums.  It only
+// applies below the persistent grid's own target (loads_per_cu / R
+// wavefronts per compute unit), so large inputs keep the full persistent grid
+// whatever the block size.  Returns `blocks` or the smaller capped count.
+uint64_t cap_small_input(uint64_t blocks, uint64_t n, const OpDefaults& d, int cu_count,
+                         uint64_t W, uint64_t R) {
+  const uint64_t cap_waves = uint64_t(std::ceil(std::sqrt(double(n)) / double(R)));
+  const uint64_t target_waves = uint64_t(cu_count) * ((uint64_t(d.loads_per_cu) + R - 1) / R);
+  if (cap_waves >= target_waves) return blocks;
+  uint64_t cap = (cap_waves + W - 1) / W;
+  if (cap < 1) cap = 1;
+  return blocks < cap ? blocks : cap;
 }
 
 // Ticket groups.  Up to kSingleLevelMax blocks use one group: the tail of
@@ -91,7 +112,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     if (n == 0) { *plan = p; return ARMX_OK; }
     const uint64_t chains = ceil_div(n, kChunk * R);
     uint64_t grid = ceil_div(chains, W);
-    const uint64_t resident = persistent_blocks(d, cu_count, W, R);
+    const uint64_t resident =
+        cap_small_input(persistent_blocks(d, cu_count, W, R), n, d, cu_count, W, R);
     if (grid > resident) grid = resident;
     if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) grid = uint64_t(c.grid_blocks);
     if (grid < 1) grid = 1;
@@ -107,7 +129,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     const uint64_t chains = ceil_div(n, kChunk * R);
     uint64_t grid = ceil_div(chains, W);
     if (!(c.flags & ARMX_FLAG_ONE_CHAIN)) {
-      const uint64_t resident = persistent_blocks(d, cu_count, W, R);
+      const uint64_t resident =
+          cap_small_input(persistent_blocks(d, cu_count, W, R), n, d, cu_count, W, R);
       if (grid > resident) grid = resident;
     }
     if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) {
@@ -138,7 +161,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.n = n;
     if (n == 0) { *plan = p; return ARMX_OK; }
     const uint64_t chunks = ceil_div(n, kChunk);
-    uint64_t target = persistent_blocks(d, cu_count, W, R);
+    uint64_t target = cap_small_input(persistent_blocks(d, cu_count, W, R), n, d, cu_count, W, R);
     if (c.grid_blocks > 0 && target > uint64_t(c.grid_blocks)) target = uint64_t(c.grid_blocks);
     if (target > uint64_t(kFixedMaxBlocks)) target = kFixedMaxBlocks;
     if (target < 1) target = 1;

@@ -103,7 +103,9 @@ typedef struct armx_config {
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
  * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth;
  * 64 / R for the MMA-levels form), and at least one block per compute
- * unit. */
+ * unit.  Inputs too small to feed that grid use about sqrt(n) / R
+ * wavefronts instead (the flat sums: fewer blocks finish sooner when each
+ * has little to stream). */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.
