@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libarmx.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["sum_kernels.hip", "fixed_kernels.hip", "rows_kernels.hip", "exact_kernels.hip",
-               "rows_fixed_kernels.hip", "levels_kernels.hip"]
+               "rows_fixed_kernels.hip", "levels_kernels.hip", "short_rows_kernels.hip"]
 HOST_SOURCES = ["api.cpp", "plan.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -53,10 +53,10 @@ void log_plan(const char* entry, const armx::Plan& p) {
   if (!log_enabled()) return;
   std::fprintf(stderr,
                "armx: %s n=%llu rows=%llu ld=%llu grid=%d block=%d R=%d flags=0x%x "
-               "mode=%d lds=%zu ws=%zu group=%u\n",
+               "mode=%d lds=%zu ws=%zu group=%u seg=%d remap=%d\n",
                entry, (unsigned long long)p.n, (unsigned long long)p.rows,
                (unsigned long long)p.ld, p.grid, p.waves * 64, p.r, p.flags, p.mode, p.lds_bytes,
-               p.ws_bytes, p.group);
+               p.ws_bytes, p.group, p.seg_log2, p.xcd_remap);
 }
 
 // Common checks of reduce_sum, reduce_sum_fixed_order and reduce_sum_exact.

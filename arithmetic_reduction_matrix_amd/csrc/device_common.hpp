@@ -38,11 +38,16 @@ __device__ __forceinline__ u32x4 load16(const u32x4* p) {
   }
 }
 
-// 8 binary16 values starting at element e of xh; elements at or beyond n are
-// replaced by `fill` (a binary16 bit pattern).  Only used for the one chunk
-// that straddles the end of the input, so scalar loads are fine here.
+// 8 binary16 values starting at element e of xh (e a multiple of 8, xh
+// 16-byte aligned); elements at or beyond n are replaced by `fill` (a
+// binary16 bit pattern).  A lane whose 8 values all lie below n makes one
+// 16-byte load, a lane entirely past n loads nothing, and only the lane that
+// straddles n reads its values one by one.
 __device__ __forceinline__ u32x4 load8_masked(const uint16_t* __restrict__ xh, uint64_t e,
                                               uint64_t n, uint32_t fill) {
+  if (e + 8 <= n) return *reinterpret_cast<const u32x4*>(xh + e);
+  const uint32_t f2 = fill | (fill << 16);
+  if (e >= n) return u32x4{f2, f2, f2, f2};
   uint32_t h[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) h[i] = (e + i < n) ? uint32_t(xh[e + i]) : fill;
@@ -52,6 +57,38 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t* __restrict__ xh, u
   v[2] = h[4] | (h[5] << 16);
   v[3] = h[6] | (h[7] << 16);
   return v;
+}
+
+// 8 binary16 values starting at element e of xh, as load8_masked, but with
+// no branch: every element is read (from index min(e + i, n - 1), so n must
+// be at least 1) and those at or past n are replaced by `fill`.  Eight 2-byte
+// loads per lane; for one-off reads outside a pipelined loop.
+__device__ __forceinline__ u32x4 load8_clamped(const uint16_t* __restrict__ xh, uint64_t e,
+                                               uint64_t n, uint32_t fill) {
+  uint32_t h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool in = e + i < n;
+    const uint32_t v = xh[in ? e + i : n - 1];
+    h[i] = in ? v : fill;
+  }
+  u32x4 v;
+  v[0] = h[0] | (h[1] << 16);
+  v[1] = h[2] | (h[3] << 16);
+  v[2] = h[4] | (h[5] << 16);
+  v[3] = h[6] | (h[7] << 16);
+  return v;
+}
+
+// Blocks are dispatched to the 8 XCDs of an MI355X round-robin (block b to
+// XCD b % 8), and every XCD has its own L2 and address-translation caches.
+// This logical block id gives each XCD a contiguous range of ids, so that
+// work assigned by consecutive ids (neighbouring rows) stays on one XCD.
+constexpr uint64_t kXcds = 8;
+__device__ __forceinline__ uint64_t xcd_block_id() {
+  const uint64_t G = gridDim.x, b = blockIdx.x;
+  const uint64_t per = G / kXcds, rem = G % kXcds, x = b % kXcds;
+  return x * per + (x < rem ? x : rem) + b / kXcds;
 }
 
 // ---- cross-lane moves -------------------------------------------------------
@@ -280,6 +317,58 @@ __device__ __forceinline__ void tail_chain(const uint16_t* __restrict__ xh, uint
     v[r] = e < len ? load8_masked(xh, e, len, 0u) : u32x4{0u, 0u, 0u, 0u};
   }
   chain_step<R, PLAIN>(v, run);
+}
+
+// ---- rows that end inside a chain --------------------------------------------
+//
+// A row-major matrix of `rows` rows of `cols` values (cols > 512) with pitch
+// ld >= cols, a multiple of 8 when there is more than one row, so every row
+// starts 16-byte aligned.  The chunk grid restarts at every row, and a row's
+// last chain of R chunks may end inside the row's last chunk or before it.
+// In such a chain, chunks past the row's last chunk read that chunk again,
+// and in the last chunk the lanes past the row read on into the pitch and
+// the next row: at most 511 values past the row, so inside the matrix for
+// every row but the last (the next row starts at most ld values on and holds
+// more than 512).  The pipelined streams therefore leave the last row of the
+// matrix to a path with exact masked loads.  The values that are not the
+// row's are replaced by `fill` in registers.
+
+// Loads chain c of the row at xr (R chunks, 16 bytes per lane each); chunks
+// past `last_chunk` read chunk `last_chunk` again.
+template <int R, bool NT>
+__device__ __forceinline__ void load_row_chain(const uint16_t* __restrict__ xr, uint64_t c,
+                                               uint64_t last_chunk, int lane, u32x4 (&v)[R]) {
+  const u32x4* p = reinterpret_cast<const u32x4*>(xr) + lane;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint64_t ci = c * R + uint64_t(r);
+    v[r] = load16<NT>(p + (ci < last_chunk ? ci : last_chunk) * 64);
+  }
+}
+
+// Replaces the values of chain c (as loaded by load_row_chain) at or past
+// cols by `fill` (a binary16 pattern).  Whole chunks are decided per chunk;
+// only the chunk that straddles cols is masked lane by lane.
+template <int R>
+__device__ __forceinline__ void mask_row_chain(u32x4 (&v)[R], uint64_t c, uint64_t cols,
+                                               uint32_t fill, int lane) {
+  const uint32_t f2 = fill | (fill << 16);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint64_t cs = (c * R + uint64_t(r)) * 512;
+    if (cs + 512 <= cols) continue;
+    if (cs >= cols) {
+      v[r] = u32x4{f2, f2, f2, f2};
+      continue;
+    }
+    const int left = int(cols - cs) - lane * 8;   // values of this lane's slot in the row
+    const int k = left < 0 ? 0 : (left > 8 ? 8 : left);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t keep = (2 * w < k ? 0xFFFFu : 0u) | (2 * w + 1 < k ? 0xFFFF0000u : 0u);
+      v[r][w] = (v[r][w] & keep) | (f2 & ~keep);
+    }
+  }
 }
 
 // The wavefront total of the running per-lane sums (valid in every lane).

@@ -69,6 +69,10 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t 
 // out[r] = balanced-tree sum of row r, r < plan.rows.
 hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStream_t stream);
 
+// out[r] = balanced-tree sum of row r, r < plan.rows, for rows of at most one
+// chunk (plan mode 2); serves both row entry points.
+hipError_t launch_short_rows(const Plan& plan, const void* x, float* out, hipStream_t stream);
+
 // out[0 .. count) = +0.0 (a small kernel rather than a memset, so the call can
 // be captured in a graph and replayed).
 hipError_t launch_zero(float* out, uint64_t count, hipStream_t stream);

@@ -50,6 +50,50 @@ uint64_t cap_small_input(uint64_t blocks, uint64_t n, const OpDefaults& d, int c
   return blocks < cap ? blocks : cap;
 }
 
+// Rows of at most one chunk (mode 2): a row takes ceil(cols / 8) lanes,
+// padded to a power of two.  Sets the mode, the lane count and the grid.
+void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
+  const uint64_t lanes = (p.n + 7) / 8;
+  int lg = 0;
+  while ((uint64_t(1) << lg) < lanes) ++lg;
+  p.mode = 2;
+  p.seg_log2 = lg;
+  const uint64_t rows_per_group = uint64_t(64) >> lg;
+  const uint64_t groups = (p.rows + rows_per_group - 1) / rows_per_group;
+  const uint64_t waves = (groups + kShortGroups - 1) / kShortGroups;
+  uint64_t grid = (waves + W - 1) / W;
+  const uint64_t resident = ceil_div(uint64_t(cu_count) * kShortWavesPerCu, W);
+  if (grid > resident) grid = resident;
+  if (grid_cap > 0 && grid > uint64_t(grid_cap)) grid = uint64_t(grid_cap);
+  p.grid = int(grid < 1 ? 1 : grid);
+}
+
+// Automatic shapes for rows longer than one chunk (cols > 512), measured on
+// MI355X with 2^28 values.  Rows of fewer than 8 chunks carry a fixed cost
+// per row (the chain's result, the row combine, the store) that more
+// wavefronts hide: they take R = 1 (16 wavefronts per compute unit) and
+// blocks of 512 threads (8 consecutive rows per block); fixed-order rows of
+// exactly 2 or 4 chunks are one group each (R = chunks).  Longer rows keep
+// the per-operation defaults.
+struct RowShape {
+  uint64_t r;
+  int block;
+};
+
+RowShape rows_auto_shape(uint64_t cols, const OpDefaults& d, bool fixed) {
+  const uint64_t chunks = ceil_div(cols, kChunk);
+  if (chunks >= 8) return {uint64_t(d.r), d.block};
+  if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
+  return {1, fixed ? 256 : 512};
+}
+
+// Consecutive rows whose pitch is not a whole number of 128-byte lines share
+// a line; with blocks dispatched round-robin over the XCDs, each XCD would
+// fetch it.  Such rows get the XCD-contiguous block order.  (Measured on
+// MI355X: 1000-value rows 85 -> 78 us; rows of whole lines gain nothing and
+// 4096-value rows lose, 74 -> 79 us.)
+int rows_remap(uint64_t rows, uint64_t ld) { return rows > 1 && ld % 64 != 0 ? 1 : 0; }
+
 // Ticket groups.  Up to kSingleLevelMax blocks use one group: the tail of
 // the kernel then has the fewest serialised memory round trips (measured
 // faster at 256 blocks).  Larger grids use a power-of-two group size near
@@ -78,6 +122,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
               const armx_config* cfg, int cu_count, Plan* plan) {
   armx_config c{};
   if (cfg) c = *cfg;
+  const bool auto_r = c.chain_r == 0;
+  const bool auto_block = c.block_threads == 0;
   const OpDefaults d = op == kOpFixed                    ? kFixedDefaults
                        : op == kOpRows                   ? kRowsDefaults
                        : op == kOpRowsFixed              ? kRowsFixedDefaults
@@ -100,7 +146,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   p.flags = c.flags;
   p.start_event = c.start_event;
   p.stop_event = c.stop_event;
-  const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
+  const uint64_t W = uint64_t(p.waves);
+  uint64_t R = uint64_t(p.r);
 
   if (op != kOpSum && (c.flags & ARMX_FLAG_MMA_LEVELS)) return ARMX_ERR_CONFIG;
   if (op == kOpExact) {
@@ -194,6 +241,22 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.rows = rows;
     p.n = cols;
     p.ld = ld;
+    p.xcd_remap = rows_remap(rows, ld);
+    if (rows > 0 && cols > 0 && cols <= kChunk) {
+      if (auto_block) p.waves = kShortBlock / 64;
+      plan_short_rows(p, cu_count, uint64_t(p.waves), c.grid_blocks);
+      p.ws_bytes = 0;
+      *plan = p;
+      return ARMX_OK;
+    }
+    uint64_t W = uint64_t(p.waves);
+    if (cols > kChunk) {
+      const RowShape a = rows_auto_shape(cols, d, false);
+      if (auto_r) R = a.r;
+      if (auto_block) W = uint64_t(a.block / 64);
+      p.r = int(R);
+      p.waves = int(W);
+    }
     // many rows: one wavefront per row over a persistent grid; few rows: a
     // block per row so that every row still gets W wavefronts
     const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
@@ -224,11 +287,25 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.n = cols;
     p.ld = ld;
     if (rows == 0 || cols == 0) { *plan = p; return ARMX_OK; }
+    p.xcd_remap = rows_remap(rows, ld);
+    if (cols <= kChunk) {
+      if (auto_block) p.waves = kShortBlock / 64;
+      plan_short_rows(p, cu_count, uint64_t(p.waves), c.grid_blocks);
+      *plan = p;
+      return ARMX_OK;
+    }
+    uint64_t W = uint64_t(p.waves);
+    {
+      const RowShape a = rows_auto_shape(cols, d, true);
+      if (auto_r) R = a.r;
+      if (auto_block) W = uint64_t(a.block / 64);
+      p.r = int(R);
+      p.waves = int(W);
+    }
     const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
     const uint64_t group_elems = R * kChunk;
     uint64_t grid;
-    if (is_pow2(R) && cols % group_elems == 0 && cols / group_elems <= 64 &&
-        (rows >= blocks * W || W == 1)) {
+    if (is_pow2(R) && ceil_div(cols, group_elems) <= 64 && (rows >= blocks * W || W == 1)) {
       // flat: a wavefront's rows stream back to back; each row is at most
       // 64 group subtrees, one per lane of a slot register
       p.mode = 1;

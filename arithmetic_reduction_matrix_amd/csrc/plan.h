@@ -69,7 +69,10 @@ struct Plan {
   unsigned flags = 0;
   int log2_chunks = 0;      // fixed order: 2^log2_chunks chunks per wavefront
   int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row;
-                            // fixed-order rows: 1 = flat (cross-row stream), 0 = general
+                            // fixed-order rows: 1 = flat (cross-row stream), 0 = general;
+                            // both: 2 = rows of at most one chunk, segmented lanes
+  int seg_log2 = 0;         // mode 2: log2 of the lanes per row (a power of two)
+  int xcd_remap = 0;        // rows: give each XCD a contiguous range of block ids
   unsigned slots_per_wave = 0;  // fixed order: LDS floats of each wavefront's node log
   size_t lds_bytes = 0;     // dynamic LDS per block
   uint64_t n = 0;           // elements (sum / fixed); columns (rows)
@@ -83,6 +86,15 @@ struct Plan {
   void* start_event = nullptr;  // hipEvent_t stamped around the main kernel
   void* stop_event = nullptr;
 };
+
+// Rows of at most one chunk (mode 2): each wavefront takes kShortGroups
+// groups of 64 / 2^seg_log2 rows per step, one 16-byte load per lane each,
+// and the persistent grid holds kShortWavesPerCu wavefronts per compute unit
+// (measured on MI355X at 2^28 values: 4 beat 2 and 8 for 64 to 512 columns,
+// best as one block of 4 wavefronts).
+constexpr int kShortGroups = 8;
+constexpr int kShortWavesPerCu = 4;
+constexpr int kShortBlock = 256;   // automatic block size for such rows
 
 // MMA levels (ARMX_FLAG_MMA_LEVELS): the number of fp32 values level `level`
 // produces from `count` inputs -- one per chain of R x 512 binary16 values at

@@ -10,14 +10,20 @@
 // choices otherwise break (same Abstract).
 //
 // Two mappings:
-//  * flat (many rows whose length is a whole number of R-chunk groups, at
-//    most 64 groups): each wavefront owns rows g, g + T, ...; it streams
-//    (row, group) items with a software pipeline that runs across rows; a
-//    group's subtree root is selected into lane (group index) of a slot
-//    register, and the row root is lane_tree_full of that register (lanes
-//    past the row's groups hold -0.0, which only passes values up), written
-//    after every group so that the last write is the complete root.  The
-//    loop body has no branches.
+//  * flat (many rows of at most 64 groups of R chunks, R a power of two):
+//    each wavefront owns rows g, g + T, ...; it streams (row, group) items
+//    with a software pipeline that runs across rows; a row's last group may
+//    end inside the row, and its values past the row are -0.0 (read and
+//    masked as load_row_chain and mask_row_chain describe; the matrix's last
+//    row then takes exact masked loads instead), so it is still the subtree
+//    of its R-aligned chunks; a group's subtree root is selected
+//    into lane (group index) of a slot register, and the row root is
+//    lane_tree_full of that register (lanes past the row's groups hold -0.0,
+//    which only passes values up), written after every group so that the
+//    last write is the complete root.  The loop body branches only around
+//    the masking of a row's last group.
+//  * rows of at most 512 values go to the segmented kernel of
+//    short_rows_kernels.hip.
 //  * general (any length): each block sums a row; its W wavefronts (W a power
 //    of two) take aligned power-of-two chunk ranges of the row and reduce
 //    them as the flat fixed-order kernel does; the W roots are combined by a
@@ -43,26 +49,32 @@ __device__ __forceinline__ float group_root(const u32x4 (&v)[R]) {
 
 template <int R, bool NT>
 __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, uint64_t rows,
-                                                uint64_t gpr, uint64_t ld,
+                                                uint64_t cols, uint64_t ld,
                                                 float* __restrict__ out, uint64_t g, uint64_t T,
                                                 int lane) {
   if (g >= rows) return;
+  const uint64_t group_elems = uint64_t(R) * 512;
+  const uint64_t gpr = (cols + group_elems - 1) / group_elems;
+  const bool partial = gpr * group_elems != cols;
+  const uint64_t last_chunk = (cols - 1) / 512;
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * gpr;
+  const uint64_t row_step = T * ld;
   uint64_t lk = 0, lc = 0;   // next (row, group) to load
   uint64_t rk = 0, rc = 0;   // next (row, group) to reduce
-  auto ptr = [&]() {
-    return reinterpret_cast<const u32x4*>(x + (g + lk * T) * ld) + lc * (uint64_t(R) * 64);
-  };
-  auto advance_load = [&]() {
+  const uint16_t* load_row = x + g * ld;
+  auto load = [&](u32x4 (&v)[R]) {
+    load_row_chain<R, NT>(load_row, lc, last_chunk, lane, v);
     // stays on the last item once it is reached (the re-read is not used)
     const bool more_in_row = lc + 1 < gpr;
     const bool more_rows = lk + 1 < K;
     lc = more_in_row ? lc + 1 : (more_rows ? 0 : lc);
     lk = more_in_row ? lk : (more_rows ? lk + 1 : lk);
+    load_row = (!more_in_row && more_rows) ? load_row + row_step : load_row;
   };
   float slots = -0.0f;
-  auto reduce = [&](const u32x4 (&v)[R]) {
+  auto reduce = [&](u32x4 (&v)[R]) {
+    if (partial && rc + 1 == gpr) mask_row_chain<R>(v, rc, cols, 0x8000u, lane);
     const float node = group_root<R>(v);
     slots = uint64_t(lane) == rc ? node : (rc == 0 ? -0.0f : slots);
     const float root = lane_tree_full(slots);
@@ -72,20 +84,60 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
     rk = row_done ? rk + 1 : rk;
   };
   u32x4 a[R], b[R];
-  load_group<R, NT>(ptr(), 0, lane, a);
-  advance_load();
+  load(a);
   uint64_t j = 0;
   for (; j + 1 < items; j += 2) {
-    load_group<R, NT>(ptr(), 0, lane, b);
-    advance_load();
+    load(b);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
     reduce(a);
-    load_group<R, NT>(ptr(), 0, lane, a);
-    advance_load();
+    load(a);
     __builtin_amdgcn_sched_barrier(0);
     reduce(b);
   }
   if (j < items) reduce(a);
+}
+
+// The root of one row of at most 64 groups, by one wavefront with no read
+// past the row: the same group subtrees and slot register as rows_fixed_flat,
+// its whole groups streamed with the same ping-pong pipeline, the partial last
+// group read with exact masked loads.
+template <int R, bool NT>
+__device__ __forceinline__ float row_root_masked(const uint16_t* __restrict__ xr, uint64_t cols,
+                                                 int lane) {
+  const uint64_t group_elems = uint64_t(R) * 512;
+  const uint64_t gpr = (cols + group_elems - 1) / group_elems;
+  const uint64_t gfull = cols / group_elems;
+  const u32x4* x4 = reinterpret_cast<const u32x4*>(xr);
+  float slots = -0.0f;
+  auto take = [&](uint64_t gi, const u32x4 (&v)[R]) {
+    const float node = group_root<R>(v);
+    slots = uint64_t(lane) == gi ? node : slots;
+  };
+  uint64_t gi = 0;
+  if (gfull > 0) {
+    u32x4 a[R], b[R];
+    load_group<R, NT>(x4, 0, lane, a);
+    for (; gi + 1 < gfull; gi += 2) {
+      load_group<R, NT>(x4, (gi + 1) * R, lane, b);
+      __builtin_amdgcn_sched_barrier(0);
+      take(gi, a);
+      load_group<R, NT>(x4, (gi + 2 < gfull ? gi + 2 : gi + 1) * R, lane, a);
+      __builtin_amdgcn_sched_barrier(0);
+      take(gi + 1, b);
+    }
+    if (gi < gfull) {
+      take(gi, a);
+      ++gi;
+    }
+  }
+  if (gi < gpr) {
+    u32x4 v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      v[r] = load8_masked(xr, (gi * R + uint64_t(r)) * 512 + uint64_t(lane) * 8, cols, 0x8000u);
+    take(gi, v);
+  }
+  return lane_tree_full(slots);
 }
 
 template <int R, bool NT>
@@ -93,16 +145,22 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
                                                           uint64_t rows, uint64_t cols,
                                                           uint64_t ld, float* __restrict__ out,
                                                           int flat, int log2c,
-                                                          unsigned slots_per_wave) {
+                                                          unsigned slots_per_wave, int remap) {
   __shared__ float red[16];
   const int lane = lane_id();
   const int W = num_waves();
 
   if (flat) {
     if constexpr (is_pow2(R)) {
-      const uint64_t gpr = cols / (uint64_t(R) * 512);
-      rows_fixed_flat<R, NT>(x, rows, gpr, ld, out, uint64_t(blockIdx.x) * W + wave_id(),
-                             uint64_t(gridDim.x) * W, lane);
+      const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + wave_id();
+      const uint64_t T = uint64_t(gridDim.x) * W;
+      // the last row stays out of the stream when rows end inside a group
+      const bool tail = cols % (uint64_t(R) * 512) != 0;
+      rows_fixed_flat<R, NT>(x, tail ? rows - 1 : rows, cols, ld, out, g, T, lane);
+      if (tail && g == (rows - 1) % T) {
+        const float root = row_root_masked<R, NT>(x + (rows - 1) * ld, cols, lane);
+        if (lane == 0) out[rows - 1] = root;
+      }
     }
     return;
   }
@@ -153,6 +211,7 @@ const void* rows_fixed_kernel_for(int r, bool nt) {
 hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
+  if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
   const void* fn = rows_fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
   if (!fn) return hipErrorInvalidValue;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
@@ -160,7 +219,8 @@ hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStr
   int flat = plan.mode;
   int log2c = plan.log2_chunks;
   unsigned slots_per_wave = plan.slots_per_wave;
-  void* args[] = {&xh, &rows, &cols, &ld, &out, &flat, &log2c, &slots_per_wave};
+  int remap = plan.xcd_remap;
+  void* args[] = {&xh, &rows, &cols, &ld, &out, &flat, &log2c, &slots_per_wave, &remap};
   return launch_main(plan, fn, args, stream);
 }
 

@@ -6,13 +6,15 @@
 // ARMX_FLAG_PLAIN, per-lane fp32 adds) and R of them chain into the fp32
 // accumulators.  A chunk never straddles two rows: the chunk grid restarts
 // at every row (rows are 16-byte aligned because ld is a multiple of 8), and
-// a row's last partial chain is masked.  The row's fp32 total is written
+// a row's last partial chain is masked.  Rows of at most 512 values go to
+// the segmented kernel of short_rows_kernels.hip instead.  The row's fp32 total is written
 // directly -- no workspace, no second pass.  Two mappings:
 //  * wave_rows: each wavefront sums whole rows (rows g, g + T, ... for
-//    wavefront g of T); when rows are whole numbers of chains the loads of
-//    the next row are issued before the current row is finished, so the
-//    pipeline runs across rows; no block synchronisation at all.  Used when
-//    there are many rows.
+//    wavefront g of T); the loads of the next row are issued before the
+//    current row is finished, so the pipeline runs across rows, and a row's
+//    last partial chain is masked in registers (the matrix's last row then
+//    takes exact masked loads instead); no block synchronisation at all.
+//    Used when there are many rows.
 //  * otherwise each block sums a row (looping over rows if needed) and its W
 //    wavefronts take the row's chains round-robin, combined through LDS.
 #include "device_common.hpp"
@@ -27,30 +29,44 @@ using namespace dev;
 // g, g + T, g + 2T, ... (k counts them) and chains 0 .. cpr-1 of each.
 struct RowCursor {
   uint64_t k = 0, c = 0;
+  __device__ __forceinline__ void next(uint64_t cpr) {
+    if (++c == cpr) {
+      c = 0;
+      ++k;
+    }
+  }
 };
 
-// The flattened stream of one wavefront's rows when every row is a whole
-// number of chains: loads run ahead across row boundaries, so the pipeline
-// never drains between rows.  At the end of a row its total is written and
-// the running sum restarts.
+// The flattened stream of one wavefront's rows (rows g, g + T, ... below
+// `rows`, which must not include the matrix's last row when rows end inside
+// a chain): loads run ahead across row boundaries, so the pipeline never
+// drains between rows.  A row that is not a whole number of chains ends in a
+// partial chain, read and masked as load_row_chain and mask_row_chain
+// describe (values past the row count as +0.0).  At the end of a row its
+// total is written and the running sum restarts.
 template <int R, bool NT, bool PLAIN>
 __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64_t rows,
-                                          uint64_t cpr, uint64_t ld, float* __restrict__ out,
+                                          uint64_t cols, uint64_t ld, float* __restrict__ out,
                                           uint64_t g, uint64_t T, int lane) {
   if (g >= rows) return;
+  const uint64_t chain_elems = uint64_t(R) * 512;
+  const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
+  const bool partial = cpr * chain_elems != cols;
+  const uint64_t last_chunk = (cols - 1) / 512;
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * cpr;
-  RowCursor pf, pr;   // next item to load, next item to reduce
-  auto ptr = [&](const RowCursor& q) {
-    return reinterpret_cast<const u32x4*>(x + (g + q.k * T) * ld) + q.c * (uint64_t(R) * 64);
-  };
-  auto advance_load = [&]() {
+  const uint64_t row_step = T * ld;
+  RowCursor pf, rd, pr;   // next item to load, to reduce, to retire
+  const uint16_t* load_row = x + g * ld;
+  auto load = [&](u32x4 (&v)[R]) {
+    load_row_chain<R, NT>(load_row, pf.c, last_chunk, lane, v);
     // stays on the last item once it is reached (the re-read is not used)
     if (pf.c + 1 < cpr) {
       ++pf.c;
     } else if (pf.k + 1 < K) {
       pf.c = 0;
       ++pf.k;
+      load_row += row_step;
     }
   };
   // A chain's value joins the running sum one half-step later (after the next
@@ -61,39 +77,50 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
     if (!have_pending) return;
     run += pending;
     have_pending = false;
-    if (++pr.c == cpr) {
+    if (pr.c + 1 == cpr) {
       const float total = wave_total<PLAIN>(run);
       if (lane == 0) out[g + pr.k * T] = total;
       run = 0.0f;
-      pr.c = 0;
-      ++pr.k;
     }
+    pr.next(cpr);
   };
-  auto reduce = [&](const u32x4 (&v)[R]) {
+  auto reduce = [&](u32x4 (&v)[R]) {
     retire();
+    if (partial && rd.c + 1 == cpr) mask_row_chain<R>(v, rd.c, cols, 0u, lane);
     pending = chain_value<R, PLAIN>(v);
     have_pending = true;
+    rd.next(cpr);
   };
   u32x4 a[R], b[R];
-  load_chain<R, NT>(ptr(pf), 0, lane, a);
-  advance_load();
+  load(a);
   for (uint64_t j = 0; j < items; j += 2) {
-    load_chain<R, NT>(ptr(pf), 0, lane, b);
-    advance_load();
+    load(b);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
     reduce(a);
-    load_chain<R, NT>(ptr(pf), 0, lane, a);
-    advance_load();
+    load(a);
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < items) reduce(b);
   }
   retire();
 }
 
+// One row summed by one wavefront with exact masked loads (no read past
+// the row): its whole chains pipelined, then the partial chain.
+template <int R, bool NT, bool PLAIN>
+__device__ __forceinline__ float row_total_masked(const uint16_t* __restrict__ xr, uint64_t cols,
+                                                  int lane) {
+  const uint64_t chains_full = cols / (uint64_t(R) * 512);
+  float run = 0.0f;
+  stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane, run);
+  if (chains_full * R * 512 < cols) tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
+  return wave_total<PLAIN>(run);
+}
+
 template <int R, bool NT, bool PLAIN>
 __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__ x, uint64_t rows,
                                                     uint64_t cols, uint64_t ld,
-                                                    float* __restrict__ out, int wave_rows) {
+                                                    float* __restrict__ out, int wave_rows,
+                                                    int remap) {
   __shared__ float red[16];
   const int lane = lane_id();
   const uint64_t W = uint64_t(num_waves());
@@ -101,20 +128,14 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
   const bool tail = chains_full * R * 512 < cols;
 
   if (wave_rows) {
-    const uint64_t total_waves = uint64_t(gridDim.x) * W;
-    const uint64_t g = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
-    if (!tail) {
-      rows_flat<R, NT, PLAIN>(x, rows, chains_full, ld, out, g, total_waves, lane);
-      return;
-    }
-    for (uint64_t row = g; row < rows; row += total_waves) {
-      const uint16_t* xr = x + row * ld;
-      float run = 0.0f;
-      stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane,
-                                  run);
-      tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
-      const float total = wave_total<PLAIN>(run);
-      if (lane == 0) out[row] = total;
+    const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + uint64_t(wave_id());
+    const uint64_t T = uint64_t(gridDim.x) * W;
+    // the last row stays out of the stream when rows end inside a chain
+    const uint64_t streamed = tail ? rows - 1 : rows;
+    rows_flat<R, NT, PLAIN>(x, streamed, cols, ld, out, g, T, lane);
+    if (tail && g == (rows - 1) % T) {
+      const float total = row_total_masked<R, NT, PLAIN>(x + (rows - 1) * ld, cols, lane);
+      if (lane == 0) out[rows - 1] = total;
     }
     return;
   }
@@ -161,13 +182,15 @@ const void* rows_kernel_for(int r, bool nt, bool plain) {
 hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
+  if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
   const void* fn = rows_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
                                    (plan.flags & ARMX_FLAG_PLAIN) != 0);
   if (!fn) return hipErrorInvalidValue;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
   int wave_rows = plan.mode;
-  void* args[] = {&xh, &rows, &cols, &ld, &out, &wave_rows};
+  int remap = plan.xcd_remap;
+  void* args[] = {&xh, &rows, &cols, &ld, &out, &wave_rows, &remap};
   return launch_main(plan, fn, args, stream);
 }
 

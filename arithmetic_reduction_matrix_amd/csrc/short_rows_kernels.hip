@@ -1,0 +1,153 @@
+// Row sums of rows no longer than one chunk (cols <= 512), for both row
+// entry points.
+//
+// A row of cols values takes P = 2^S lanes, the power of two at or above
+// ceil(cols / 8), one 16-byte slot of 8 values each; a wavefront load then
+// covers a group of 64 / P rows, and a wavefront takes kShortGroups groups per
+// step.  The chunk grid of the longer-row kernels would give every such row a
+// whole 512-value load of its own, mostly masked; here every lane of every load
+// carries data whenever cols fills its P slots.
+//
+// Each lane's 8 values are levels 1-3 of the row's balanced tree (the leaves
+// widened exactly to binary32, padded with -0.0, every node one binary32
+// round-to-nearest-even addition: "Taming Bitwise Behavior in GPU Kernels with
+// Tensor Core", arXiv 2609.11356, Abstract), and the row's P lanes are levels
+// 4 to 3 + S by the lane ladder, so every lane of a row ends with the row's
+// root.  The result is the row's fixed-order sum, which is also a valid
+// free-order sum: the all-ones MFMA of "GPU Tensor Cores for fast Arithmetic
+// Reductions" (arXiv 2001.05585, Abstract) adds values of lanes 16 apart,
+// which here belong to different rows, so it is not used for these rows.
+//
+// The loop body has no branches.  Every load is unconditional: a lane past
+// the row's last slot reads the last slot again, a row past the end reads the
+// last row the loop covers, and values that are not the row's are replaced by
+// -0.0 with per-lane masks.  Those re-read rows are reduced like the real
+// ones and write the same value to the same place.  A slot that straddles the
+// end of the row reads 16 bytes of which the tail lies in the row's pitch
+// (ld is a multiple of 8 when there is more than one row); only the last row
+// of a matrix whose cols is not a multiple of 8 could end inside such a slot,
+// so that row is summed apart, with element loads.
+#include "fixed_tree.hpp"
+#include "launch.h"
+
+namespace armx {
+namespace {
+
+using namespace dev;
+using namespace dev::tree;
+
+constexpr uint32_t kNegZero2 = 0x80008000u;
+
+// Levels 1-3 of the tree over one lane's 8 values.
+__device__ __forceinline__ float leaf8(u32x4 t) {
+  const float b0 = pair_node(t[0]) + pair_node(t[1]);
+  const float b1 = pair_node(t[2]) + pair_node(t[3]);
+  return b0 + b1;
+}
+
+template <int S, bool NT>
+__global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __restrict__ x,
+                                                          uint64_t rows, uint64_t cols,
+                                                          uint64_t ld, float* __restrict__ out,
+                                                          int remap) {
+  constexpr uint64_t P = uint64_t(1) << S;
+  constexpr int G = kShortGroups;
+  constexpr uint64_t RPG = 64 >> S;   // rows per group (one wavefront load)
+  constexpr uint64_t RPS = RPG * G;   // rows per step
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + uint64_t(wave_id());
+  const uint64_t T = uint64_t(gridDim.x) * W;
+  const uint64_t slot = uint64_t(lane) & (P - 1);
+  const uint64_t sub = uint64_t(lane) >> S;
+  const uint64_t last_slot = (cols - 1) / 8;
+  const uint64_t read_slot = slot < last_slot ? slot : last_slot;
+
+  // halves of this lane's slot that hold the row's values
+  const uint64_t e = slot * 8;
+  const uint64_t k = e >= cols ? 0 : (cols - e >= 8 ? 8 : cols - e);
+  u32x4 keep;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    keep[w] = (uint64_t(2 * w) < k ? 0xFFFFu : 0u) | (uint64_t(2 * w + 1) < k ? 0xFFFF0000u : 0u);
+
+  const bool ragged = (cols % 8) != 0;
+  const uint64_t body = ragged ? rows - 1 : rows;   // rows read with whole slots
+  if (ragged && g == T - 1) {
+    const uint16_t* xr = x + (rows - 1) * ld;
+    const float root = lane_tree(leaf8(load8_clamped(xr, e, cols, 0x8000u)), S);
+    if (lane == 0) out[rows - 1] = root;
+  }
+
+  const uint64_t steps = (body + RPS - 1) / RPS;
+  if (g >= steps) return;
+  const uint64_t K = (steps - 1 - g) / T + 1;   // this wavefront's steps
+  auto row_of = [&](uint64_t c, int u) {
+    const uint64_t r = c * RPS + uint64_t(u) * RPG + sub;
+    return r < body ? r : body - 1;
+  };
+  auto load_step = [&](uint64_t c, u32x4 (&v)[G]) {
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+      v[u] = load16<NT>(reinterpret_cast<const u32x4*>(x + row_of(c, u) * ld) + read_slot);
+  };
+  auto reduce_step = [&](uint64_t c, const u32x4 (&v)[G]) {
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      u32x4 t;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t[w] = (v[u][w] & keep[w]) | (kNegZero2 & ~keep[w]);
+      out[row_of(c, u)] = lane_tree(leaf8(t), S);   // every lane of the row: the same value
+    }
+  };
+  auto step = [&](uint64_t j) { return g + (j < K ? j : K - 1) * T; };
+
+  // Software pipeline with ping-pong buffers, as in the flat kernels: the next
+  // step's loads are issued before the current step is reduced; past the last
+  // step the loads and the reduction repeat it.
+  u32x4 a[G], b[G];
+  load_step(step(0), a);
+  for (uint64_t j = 0; j < K; j += 2) {
+    load_step(step(j + 1), b);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce_step(step(j), a);
+    load_step(step(j + 2), a);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce_step(step(j + 1), b);
+  }
+}
+
+template <int S>
+const void* pick_short(bool nt) {
+  return nt ? reinterpret_cast<const void*>(&short_rows_kernel<S, true>)
+            : reinterpret_cast<const void*>(&short_rows_kernel<S, false>);
+}
+
+const void* short_rows_kernel_for(int s, bool nt) {
+  switch (s) {
+    case 0: return pick_short<0>(nt);
+    case 1: return pick_short<1>(nt);
+    case 2: return pick_short<2>(nt);
+    case 3: return pick_short<3>(nt);
+    case 4: return pick_short<4>(nt);
+    case 5: return pick_short<5>(nt);
+    case 6: return pick_short<6>(nt);
+    default: return nullptr;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_short_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
+  if (plan.rows == 0) return hipSuccess;
+  if (plan.n == 0 || plan.n > kChunk) return hipErrorInvalidValue;
+  const void* fn = short_rows_kernel_for(plan.seg_log2, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  if (!fn) return hipErrorInvalidValue;
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
+  int remap = plan.xcd_remap;
+  void* args[] = {&xh, &rows, &cols, &ld, &out, &remap};
+  return launch_main(plan, fn, args, stream);
+}
+
+}  // namespace armx

@@ -267,6 +267,17 @@ def main() -> int:
                                                                              out=rout), 200)
         var["rows_fixed_order_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
         del rbufs
+        # short and ragged rows: the headline buffers viewed as matrices;
+        # bytes counted are the reads plus the fp32 results
+        for cols in (64, 1000):
+            nrows = n // cols
+            views = [b[: nrows * cols].view(nrows, cols) for b in bufs]
+            vout = torch.empty(nrows, dtype=torch.float32, device=dev)
+            moved = 2 * nrows * cols + 4 * nrows
+            for tag, fn in (("rows", armx.reduce_rows), ("rows_fixed_order", armx.reduce_rows_fixed_order)):
+                ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
+                var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
+            del views, vout
         record["variants"] = var
 
     if args.copy_calibration:

@@ -105,7 +105,14 @@ typedef struct armx_config {
  * 64 / R for the MMA-levels form), and at least one block per compute
  * unit.  Inputs too small to feed that grid use about sqrt(n) / R
  * wavefronts instead (the flat sums: fewer blocks finish sooner when each
- * has little to stream). */
+ * has little to stream).
+ * The row entry points pick their defaults by row length: rows of at most
+ * 512 values take the segmented kernel (block 256, 4 wavefronts per compute
+ * unit; chain_r has no effect there); rows of 513 to 3584 values take R = 1
+ * and blocks of 512 threads (fixed order: R = 2 or 4 and 512 threads when a
+ * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
+ * rows the defaults above.  An explicit block_threads or chain_r overrides
+ * its part. */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.
@@ -160,6 +167,14 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
  * ws       unused (armx_workspace_bytes returns 0); may be NULL.
  * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
+ *
+ * Rows of at most 512 values are summed by lanes (each row on a
+ * power-of-two group of lanes, several rows per wavefront load) in the
+ * balanced-tree order of reduce_rows_fixed_order, with or without
+ * ARMX_FLAG_PLAIN: an all-ones MFMA would add values of lanes 16 apart,
+ * which there belong to different rows.  Reads may cover the pitch padding
+ * of a row (never past the last row's cols values); its contents never
+ * reach the result.
  */
 int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out,
                 void* ws, size_t ws_bytes, const armx_config* cfg, void* stream);

@@ -43,3 +43,21 @@ def check_free_order(got: float, e, what: str = "") -> float:
     err = abs(Fraction(got) - Fraction(e.q, 1 << 24))
     assert float(err) <= REL * free_order_scale(e), (what, got, e.f64, float(err))
     return float(err) / abs(e.f64) if e.f64 else 0.0
+
+
+NAN16 = np.uint16(0x7E00)
+INF16 = np.uint16(0x7C00)
+
+
+def strided(x, ld, junk=NAN16, tail=64):
+    """Device view of x with row pitch ld, built in a flat buffer of exactly
+    (rows - 1) * ld + cols values plus `tail` more; every value that is not
+    part of a row (the padding of each pitch and the tail) holds `junk`."""
+    import torch
+    rows, cols = x.shape
+    size = (rows - 1) * ld + cols if rows else 0
+    flat = np.full(size + tail, junk, np.uint16)
+    for r in range(rows):
+        flat[r * ld:r * ld + cols] = x[r].view(np.uint16)
+    buf = torch.from_numpy(flat.view(np.float16)).to("cuda")
+    return torch.as_strided(buf, (rows, cols), (ld, 1))

@@ -128,12 +128,25 @@ int main(int argc, char** argv) {
       if (p.rows == 0 || p.n == 0) continue;
       EXPECT(p.grid >= 1 && uint64_t(p.grid) <= (uint64_t(1) << 20), "rows grid %d", p.grid);
       if (p.rows > 1) EXPECT(p.ld % 8 == 0, "pitch");
+      EXPECT(p.xcd_remap == (p.rows > 1 && p.ld % 64 != 0 ? 1 : 0), "remap %d", p.xcd_remap);
+      // rows of at most one chunk take the segmented kernel, with the
+      // smallest power-of-two lane count that holds a row
+      EXPECT((p.mode == 2) == (p.n <= 512), "short-row mode %d for %llu columns", p.mode,
+             (unsigned long long)p.n);
+      if (p.mode == 2) {
+        const uint64_t lanes = cdiv(p.n, 8), P = uint64_t(1) << p.seg_log2;
+        EXPECT(p.seg_log2 >= 0 && p.seg_log2 <= 6, "seg_log2 %d", p.seg_log2);
+        EXPECT(P >= lanes && (P == 1 || P / 2 < lanes), "lanes per row");
+        const uint64_t steps = cdiv(p.rows, (64 / P) * armx::kShortGroups);
+        EXPECT(uint64_t(p.grid) <= cdiv(steps, W), "short-row grid %d", p.grid);
+        EXPECT(p.lds_bytes == 0, "short-row lds");
+      }
     }
     if (op == ARMX_OP_ROWS_FIXED) {
       EXPECT(pow2(W), "rows fixed W");
       if (p.mode == 1) {
-        EXPECT(pow2(R) && p.n % (512 * R) == 0 && p.n / (512 * R) <= 64, "flat shape");
-      } else {
+        EXPECT(pow2(R) && cdiv(p.n, 512 * R) <= 64, "flat shape");
+      } else if (p.mode == 0) {
         EXPECT((W << p.log2_chunks) >= cdiv(p.n, 512), "rows fixed coverage");
         EXPECT(p.lds_bytes <= armx::kFixedLdsBytes, "rows fixed lds");
         EXPECT(p.lds_bytes == W * p.slots_per_wave * sizeof(float), "rows fixed lds size");

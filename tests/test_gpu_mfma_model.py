@@ -3,9 +3,9 @@
 as "Taming Bitwise Behavior in GPU Kernels with Tensor Core" (arXiv
 2609.11356, Abstract) does for closed libraries.
 
-A row of reduce_rows with R x 512 values whose only non-zero values sit in
-MFMA column 0 returns exactly that column's chain of R MFMAs: the other 15
-column sums are zero and the cross-lane combine only adds zeros.  Column 0's
+A row of reduce_rows with R x 512 values (then a chain of zeros) whose only
+non-zero values sit in MFMA column 0 returns exactly that column's chain of R
+MFMAs: the other 15 column sums are zero and the combines only add zeros.  Column 0's
 K position k is element (k // 8) * 128 + k % 8 of each 512-value tile (lane
 16 (k // 8) holds K values 8 (k // 8) .. + 7 of column 0)."""
 import numpy as np
@@ -30,9 +30,12 @@ def _gpu():
 
 
 def gpu_chains(tiles: np.ndarray) -> np.ndarray:
-    """tiles: (n, R, 32) binary16 K values of column 0 -> (n,) binary32."""
+    """tiles: (n, R, 32) binary16 K values of column 0 -> (n,) binary32.
+    Each row is the chain's R tiles and then one more chain of zeros: rows of
+    at most 512 values would take the MFMA-free short-row kernel, and adding
+    the zero chain's +0.0 to the chain value is exact."""
     n, R, _ = tiles.shape
-    x = np.zeros((n, 512 * R), np.float16)
+    x = np.zeros((n, 512 * (R + 1)), np.float16)
     for r in range(R):
         x[:, r * 512 + KPOS] = tiles[:, r, :]
     return armx.reduce_rows(to_dev(x), chain_r=R, block_threads=64).cpu().numpy()
