@@ -37,6 +37,36 @@ int main(int argc, char** argv) {
       default: return rng();
     }
   };
+  // fixed cases: the automatic row shapes
+  {
+    struct Case {
+      int op;
+      uint64_t rows, cols, ld;
+      int mode, seg_log2, waves, r, remap;
+    } cases[] = {
+        {ARMX_OP_ROWS, 100000, 64, 64, 2, 3, 4, -1, 0},
+        {ARMX_OP_ROWS_FIXED, 100000, 100, 104, 2, 4, 4, -1, 1},
+        {ARMX_OP_ROWS, 100000, 8, 8, 2, 0, 4, -1, 1},
+        {ARMX_OP_ROWS, 100000, 512, 512, 2, 6, 4, -1, 0},
+        {ARMX_OP_ROWS, 300000, 1000, 1000, 1, 0, 8, 1, 1},
+        {ARMX_OP_ROWS_FIXED, 300000, 1000, 1000, 1, 0, 4, 1, 1},
+        {ARMX_OP_ROWS_FIXED, 300000, 1024, 1024, 1, 0, 8, 2, 0},
+        {ARMX_OP_ROWS_FIXED, 300000, 2048, 2048, 1, 0, 8, 4, 0},
+        {ARMX_OP_ROWS, 65536, 4096, 4096, 1, 0, 1, 8, 0},
+        {ARMX_OP_ROWS_FIXED, 65536, 4096, 4096, 1, 0, 1, 4, 0},
+        {ARMX_OP_ROWS, 4096, 65536, 65536, 1, 0, 1, 8, 0},
+    };
+    for (const Case& k : cases) {
+      Plan p;
+      const int st = armx::make_plan(k.op, k.rows, k.cols, k.ld, nullptr, 256, &p);
+      EXPECT(st == ARMX_OK, "fixed case status %d", st);
+      EXPECT(p.mode == k.mode && p.seg_log2 == k.seg_log2 && p.waves == k.waves &&
+                 (k.r < 0 || p.r == k.r) && p.xcd_remap == k.remap,
+             "op %d %llux%llu ld %llu: mode %d seg %d waves %d r %d remap %d", k.op,
+             (unsigned long long)k.rows, (unsigned long long)k.cols, (unsigned long long)k.ld,
+             p.mode, p.seg_log2, p.waves, p.r, p.xcd_remap);
+    }
+  }
   int accepted = 0;
   for (int it = 0; it < iters; ++it) {
     const int op = int(rng() % 6);  // 5 is not an operation

@@ -27,6 +27,16 @@ def test_graph_capture_and_replay():
     n = (1 << 22) + 5
     pool = [to_dev(si.generate("uniform11", n, seed=100 + i)) for i in range(5)]
     rpool = [to_dev(si.generate_rows("normal", 256, 4096, seed=200 + i)) for i in range(5)]
+    # short rows (100 values, pitch 104) and ragged rows (1000 values)
+    spool = [to_dev(si.generate_rows("uniform11", 3000, 104, seed=400 + i)) for i in range(5)]
+    gpool = [to_dev(si.generate_rows("uniform11", 5000, 1000, seed=500 + i)) for i in range(5)]
+    sm = torch.empty_like(spool[0])
+    gm = torch.empty_like(gpool[0])
+    sv = sm[:, :100]
+    o_srows = torch.empty(3000, dtype=torch.float32, device="cuda")
+    o_sfix = torch.empty(3000, dtype=torch.float32, device="cuda")
+    o_grows = torch.empty(5000, dtype=torch.float32, device="cuda")
+    o_gfix = torch.empty(5000, dtype=torch.float32, device="cuda")
     x = torch.empty_like(pool[0])
     m = torch.empty_like(rpool[0])
     x.copy_(pool[0])
@@ -51,6 +61,10 @@ def test_graph_capture_and_replay():
         armx.reduce_rows_fixed_order(m, out=o_rfix)
         armx.reduce_sum_exact(x, out=o_ex, fixed=o_exq, workspace=ws_ex)
         armx.reduce_sum(x, out=o_lv, workspace=ws_lv, mma_levels=True)
+        armx.reduce_rows(sv, out=o_srows)
+        armx.reduce_rows_fixed_order(sv, out=o_sfix)
+        armx.reduce_rows(gm, out=o_grows)
+        armx.reduce_rows_fixed_order(gm, out=o_gfix)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -66,6 +80,8 @@ def test_graph_capture_and_replay():
     for rep in range(5):
         x.copy_(pool[rep])           # eager work between replays
         m.copy_(rpool[rep])
+        sm.copy_(spool[rep])
+        gm.copy_(gpool[rep])
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -86,6 +102,9 @@ def test_graph_capture_and_replay():
         assert np.array_equal(got[3], _bits(e_rfix)), rep
         assert np.array_equal(got[4], _bits(e_ex)), rep
         assert np.array_equal(got[5], _bits(e_lv)), rep
+        for o, fn, mat in ((o_srows, armx.reduce_rows, sv), (o_sfix, armx.reduce_rows_fixed_order, sv),
+                           (o_grows, armx.reduce_rows, gm), (o_gfix, armx.reduce_rows_fixed_order, gm)):
+            assert np.array_equal(_bits(o), _bits(fn(mat))), (rep, fn.__name__, tuple(mat.shape))
         if rep in (0, 4):
             xh = pool[rep].cpu().numpy()
             e = exact_sum(xh)

@@ -8,7 +8,11 @@ values are closed forms:
                is the binary32 nearest to 2^32 + 8198 -> 2^32 + 8192;
   free order   within the free-order gate of 2^32 + 8198;
   rows         65537 rows of 65536 (2^32 + 65536 values): every row of ones
-               sums to 65536 exactly, the last row (twos) to 131072."""
+               sums to 65536 exactly, the last row (twos) to 131072;
+  short rows   2^26 + 1 rows of 60 values at pitch 64 (the pitch padding also
+               ones): 60 per row, 120 for the last row (twos);
+  ragged rows  4294968 rows of 1000 values (past 2^32 values): 1000 per row,
+               2000 for the last row (twos)."""
 import numpy as np
 import pytest
 import torch
@@ -63,4 +67,19 @@ def test_rows_past_2p32():
         got = fn(m, **cfg)
         assert torch.equal(got, want), (fn.__name__, cfg)
     del m
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("rows,cols,ld", [((1 << 26) + 1, 60, 64), (4294968, 1000, 1000)])
+def test_short_and_ragged_rows_past_2p32(rows, cols, ld):
+    require_gpu()
+    buf = torch.ones((rows, ld), dtype=torch.float16, device="cuda")
+    buf[-1] = 2.0
+    m = buf[:, :cols]
+    want = torch.full((rows,), float(cols), device="cuda")
+    want[-1] = 2.0 * cols
+    for fn in (armx.reduce_rows, armx.reduce_rows_fixed_order):
+        got = fn(m)
+        assert torch.equal(got, want), (fn.__name__, rows, cols, ld)
+    del buf, m
     torch.cuda.empty_cache()
