@@ -245,6 +245,21 @@ def main() -> int:
                                             "launches": mma_levels_count(n, r),
                                             "vs_single_launch": avg_ms / ms}
 
+        # the small and the large single sums: 2^20 (2 MiB, cache-resident,
+        # latency-bound) and 2^30 (2 GiB; timing only, so its values are drawn
+        # on the device rather than by the seeded generator)
+        xs = [torch.from_numpy(si.workload("sum_2p20_u01")).to(dev)]
+        xs.append(xs[0].clone())
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum(xs[i & 1]), 500)
+        var["sum_2p20"] = {"ms": ms, "median_ms": med, "gbs": 2 * (1 << 20) / ms / 1e6}
+        del xs
+        xl = torch.empty(1 << 30, dtype=torch.float16, device=dev).uniform_(-1, 1)
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum(xl), 50)
+        var["sum_2p30"] = {"ms": ms, "gbs": 2 * (1 << 30) / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(xl), 50)
+        var["exact_2p30"] = {"ms": ms, "gbs": 2 * (1 << 30) / ms / 1e6}
+        del xl
+
         xf_np = si.workload("fixed_2p26_u11")
         fbufs = [torch.from_numpy(xf_np).to(dev)]
         fbufs += [fbufs[0].clone() for _ in range(3)]
