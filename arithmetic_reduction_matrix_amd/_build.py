@@ -1,4 +1,5 @@
-"""Builds libarmx.so (the HIP kernels and the C entry points) for gfx950.
+"""Builds libarmx.so (the HIP kernels and the C entry points) for gfx950, and
+libarmx_probe.so (a plain read stream, for measurement only).
 
 Run ``python -m arithmetic_reduction_matrix_amd._build`` or call ``build()``.
 Every source is compiled each time; objects go to ``_build/`` next to this
@@ -18,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libarmx.so")
+# measurement only: the plain read stream the reductions are compared with
+PROBE_LIB = os.path.join(PKG, "libarmx_probe.so")
+PROBE_SOURCES = ["read_probe.hip"]
 
 ARCH = "gfx950"
 HIP_SOURCES = ["sum_kernels.hip", "fixed_kernels.hip", "rows_kernels.hip", "exact_kernels.hip",
@@ -67,11 +71,17 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         cmds.append([hipcc, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+    probe_objs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        probe_objs.append(obj)
+        cmds.append([hipcc, *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as pool:
         list(pool.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    for out, parts in ((LIB, objs), (PROBE_LIB, probe_objs)):
+        tmp = out + ".tmp"
+        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *parts, "-o", tmp], verbose)
+        os.replace(tmp, out)
     return LIB
 
 

@@ -225,6 +225,25 @@ __device__ __forceinline__ void plain_add8(float& a, float& b, u32x4 t) {
   b += hi_f32(t[3]);
 }
 
+// ---- request pacing -----------------------------------------------------------
+//
+// Measured on MI355X: a long persistent stream reads HBM faster when each
+// wavefront pauses for a moment after reducing a chain, before issuing the
+// next chain's loads -- with slightly fewer requests outstanding at once the
+// memory system loses less to contention.  The pause is s_sleep PACE (about
+// 64 PACE clocks); it changes no arithmetic.  2^28 MFMA sum: 76.8 us without,
+// 74.9 us at PACE 8; fixed order at 2^30: 339 us without, 296 us at PACE 2.
+// Short streams lose by it (the ramp and the tail dominate), so callers pick
+// PACE from a wavefront's chain count.
+template <int PACE>
+__device__ __forceinline__ void pace_pause() {
+  if constexpr (PACE > 0) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_sleep(PACE);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // ---- streaming chains of tiles ----------------------------------------------
 
 // Loads chain c of R chunks: R x 16 bytes per lane from base + c * R chunks.
@@ -273,7 +292,8 @@ __device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
 // re-reads that chain (still in L2) and its values are not used.  A chain's
 // value is added into `run` one half-step later, after the next loads are
 // issued, so the wait for the MFMA chain's result never delays a prefetch.
-template <int R, bool NT, bool PLAIN>
+// PACE > 0 pauses after every chain (pace_pause).
+template <int R, bool NT, bool PLAIN, int PACE = 0>
 __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, uint64_t c0,
                                               uint64_t iters, uint64_t stride, int lane,
                                               float& run) {
@@ -295,12 +315,14 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
     run += pending;
     pending = chain_value<R, PLAIN>(a);
+    pace_pause<PACE>();
     load_chain<R, NT>(base, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, a);
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < iters) {
       run += pending;
       pending = chain_value<R, PLAIN>(b);
     }
+    pace_pause<PACE>();
   }
   run += pending;
 }

@@ -58,9 +58,14 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
   const uint64_t valid = first >= chunks ? 0 : (chunks - first < span ? chunks - first : span);
 
   // This wavefront's node log in dynamic LDS (`slots_per_wave` floats each).
+  // Long ranges pace their stream (pace_pause; measured on MI355X: PACE 2 from
+  // 64 groups of R chunks per wavefront).
   extern __shared__ float node_lds[];
-  const float wave_root = wave_range_root<R, NT>(x, n, first, valid, lane,
-                                                 node_lds + unsigned(wave_id()) * slots_per_wave);
+  float* log_rows = node_lds + unsigned(wave_id()) * slots_per_wave;
+  const float wave_root =
+      valid / R >= kPaceLongChains
+          ? wave_range_root<R, NT, 2>(x, n, first, valid, lane, log_rows)
+          : wave_range_root<R, NT>(x, n, first, valid, lane, log_rows);
 
   // block: W consecutive wavefront subtrees -> one subtree
   __syncthreads();

@@ -244,7 +244,7 @@ __device__ inline float wave_tree(float* vals, unsigned count, int lane) {
 // array x (leaves past n read as -0.0), by one wavefront (every lane returns
 // it); the range must be the valid prefix of an aligned power-of-two range.
 // `log_rows` is this wavefront's LDS node log.
-template <int R, bool NT>
+template <int R, bool NT, int PACE = 0>
 __device__ __forceinline__ float wave_range_root(const u32x4* __restrict__ x, uint64_t n,
                                                  uint64_t first, uint64_t valid, int lane,
                                                  float* log_rows) {
@@ -267,9 +267,11 @@ __device__ __forceinline__ float wave_range_root(const u32x4* __restrict__ x, ui
       load_group<R, NT>(x, first + (g + 1) * R, lane, b);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
       reduce_group<R>(a, log, lane);
+      pace_pause<PACE>();
       load_group<R, NT>(x, first + (g + 2 < groups ? g + 2 : g + 1) * R, lane, a);
       __builtin_amdgcn_sched_barrier(0);
       reduce_group<R>(b, log, lane);
+      pace_pause<PACE>();
     }
     if (g < groups) {
       reduce_group<R>(a, log, lane);

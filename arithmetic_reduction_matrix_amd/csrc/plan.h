@@ -87,6 +87,12 @@ struct Plan {
   void* stop_event = nullptr;
 };
 
+// Request pacing (device_common.hpp, pace_pause): streams of at least
+// kPaceLongChains chains (or groups) per wavefront take the long pause,
+// those of at least kPaceShortChains the short one.
+constexpr uint64_t kPaceLongChains = 64;
+constexpr uint64_t kPaceShortChains = 8;
+
 // Rows of at most one chunk (mode 2): each wavefront takes kShortGroups
 // groups of 64 / 2^seg_log2 rows per step, one 16-byte load per lane each,
 // and the persistent grid holds kShortWavesPerCu wavefronts per compute unit

@@ -59,7 +59,15 @@ __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, 
 
   float run = 0.0f;
   const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
-  stream_chains<R, NT, PLAIN>(x, c, iters, total_waves, lane, run);
+  // pacing (pace_pause), measured on MI355X: MFMA design 8 from 64 chains per
+  // wavefront, 2 from 8; MFMA-free design 4 from 64 chains
+  if (iters >= kPaceLongChains) {
+    stream_chains<R, NT, PLAIN, PLAIN ? 4 : 8>(x, c, iters, total_waves, lane, run);
+  } else if (!PLAIN && iters >= kPaceShortChains) {
+    stream_chains<R, NT, PLAIN, 2>(x, c, iters, total_waves, lane, run);
+  } else {
+    stream_chains<R, NT, PLAIN>(x, c, iters, total_waves, lane, run);
+  }
   c += iters * total_waves;
   if (c == chains_full && chains_full * R * 512 < n) {
     // the partial chain at the end: values past n read as +0.0

@@ -83,6 +83,48 @@ def event_timed(torch, fn, iters: int, warmup: int = 5):
     return sum(times) / len(times), times[len(times) // 2]
 
 
+def read_ceiling(torch, bufs, n: int, cus: int, iters: int = 20):
+    """Best HBM read rate of the plain load stream of libarmx_probe.so over a
+    sweep of launch shapes (dispatch-stamped events, inputs rotated), in GB/s,
+    and the shape that reached it."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "arithmetic_reduction_matrix_amd", "libarmx_probe.so"))
+    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.armx_probe_read.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, vp, vp, vp]
+    lib.armx_probe_read.restype = ci
+    words = 16 * 1024 * cus
+    out = torch.empty(words, dtype=torch.int32, device=bufs[0].device)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for s_ev, e_ev in evs:
+        s_ev.record()
+        e_ev.record()
+    shapes = [(64, k) for k in (1, 2, 4, 8, 16)] + [(256, k) for k in (1, 2, 4)] + [(1024, 1)]
+    results = []
+    for block, per_cu in shapes:
+        for loads in (4, 8, 16):
+            for nt in (1, 0):
+                def call(i, ev=(None, None)):
+                    st = lib.armx_probe_read(bufs[i & 1].data_ptr(), n, out.data_ptr(), words,
+                                             cus * per_cu, block, loads, nt,
+                                             ev[0].cuda_event if ev[0] else None,
+                                             ev[1].cuda_event if ev[1] else None, stream)
+                    if st != 0:
+                        raise RuntimeError(f"armx_probe_read returned {st}")
+                for i in range(3):
+                    call(i)
+                for i, ev in enumerate(evs):
+                    call(i, ev)
+                torch.cuda.synchronize()
+                ms = sum(a.elapsed_time(b) for a, b in evs) / iters
+                results.append((2 * n / (ms * 1e-3) / 1e9, dict(
+                    block_threads=block, blocks=cus * per_cu, waves_per_cu=per_cu * block // 64,
+                    loads=loads, nontemporal=bool(nt), launch_ms_avg=ms)))
+    results.sort(key=lambda r: -r[0])
+    return results[0]
+
+
 def mma_levels_count(n: int, r: int) -> int:
     """Launches of the MMA-levels form: one value per R x 512 inputs at level
     1, per R x 256 values above, until one value is left."""
@@ -127,6 +169,8 @@ def main() -> int:
                          "over n = 2^lo .. 2^hi (level count vs time)")
     ap.add_argument("--levels-log2", default="9-28",
                     help="lo-hi: the sizes of --levels-sweep (default 9-28)")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the sweep of the plain read-stream probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy (torch) five times, the "
                          "known-size reference for HBM byte counters")
@@ -222,6 +266,16 @@ def main() -> int:
         },
         "result": result,
     }
+
+    # ---- the achievable read rate on this device -------------------------------
+    if not args.no_read_ceiling:
+        ceil_gbs, ceil_cfg = read_ceiling(torch, bufs, n, props.multi_processor_count)
+        record["read_ceiling"] = {
+            "gbs": ceil_gbs, "frac_of_peak": ceil_gbs / HBM_PEAK_GBS,
+            "headline_frac_of_ceiling": achieved / ceil_gbs,
+            "kernel": "read_probe_kernel (libarmx_probe.so): 16-byte loads, one XOR per word",
+            "best_shape": ceil_cfg,
+        }
 
     # ---- the other rows of the hot path ---------------------------------------
     if not args.no_variants:

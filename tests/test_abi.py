@@ -12,8 +12,12 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
                       "include", "armx.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(os.path.dirname(HEADER), "armx_probe.h")
+PROBE_LIB = os.path.join(os.path.dirname(armx.LIB_PATH), "libarmx_probe.so")
+
+
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
 
@@ -207,3 +211,23 @@ def test_python_layer_type_checks():
         armx.reduce_sum(torch.zeros(8, dtype=torch.float16))      # not on a GPU
     with pytest.raises(ValueError):
         armx.reduce_rows(torch.zeros(2, 8, dtype=torch.float16))
+
+
+def test_probe_library_exports_its_symbols_and_checks_arguments():
+    # the read-stream probe (measurement only) rejects bad arguments before
+    # any HIP call, so these run without a GPU
+    lib = ctypes.CDLL(PROBE_LIB)
+    names = _declared_functions(PROBE_HEADER)
+    assert names == ["armx_probe_read"]
+    f = lib.armx_probe_read
+    vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    f.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, vp, vp, vp]
+    f.restype = ci
+    fake, words = 1 << 20, 1 << 20
+    assert f(None, 4096, fake, words, 1, 64, 8, 1, None, None, None) == -1
+    assert f(fake + 8, 4096, fake, words, 1, 64, 8, 1, None, None, None) == -2
+    assert f(fake, 4096, fake, words, 1, 96, 8, 1, None, None, None) == -3
+    assert f(fake, 4096, fake, words, 0, 64, 8, 1, None, None, None) == -3
+    assert f(fake, 4096, fake, words, 1, 64, 3, 1, None, None, None) == -3
+    assert f(fake, 4096 + 512, fake, words, 1, 64, 8, 1, None, None, None) == -5
+    assert f(fake, 4096, fake, 63, 1, 64, 8, 1, None, None, None) == -5
