@@ -90,7 +90,7 @@ def read_ceiling(torch, bufs, n: int, cus: int, iters: int = 20):
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "arithmetic_reduction_matrix_amd", "libarmx_probe.so"))
     vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    lib.armx_probe_read.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, vp, vp, vp]
+    lib.armx_probe_read.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, ci, vp, vp, vp]
     lib.armx_probe_read.restype = ci
     words = 16 * 1024 * cus
     out = torch.empty(words, dtype=torch.int32, device=bufs[0].device)
@@ -102,25 +102,26 @@ def read_ceiling(torch, bufs, n: int, cus: int, iters: int = 20):
         e_ev.record()
     shapes = [(64, k) for k in (1, 2, 4, 8, 16)] + [(256, k) for k in (1, 2, 4)] + [(1024, 1)]
     results = []
+    kinds = [(loads, nt, 0) for loads in (4, 8, 16) for nt in (1, 0)]
+    kinds += [(loads, 1, pause) for loads in (4, 8, 16) for pause in (2, 4, 8)]
     for block, per_cu in shapes:
-        for loads in (4, 8, 16):
-            for nt in (1, 0):
-                def call(i, ev=(None, None)):
-                    st = lib.armx_probe_read(bufs[i & 1].data_ptr(), n, out.data_ptr(), words,
-                                             cus * per_cu, block, loads, nt,
-                                             ev[0].cuda_event if ev[0] else None,
-                                             ev[1].cuda_event if ev[1] else None, stream)
-                    if st != 0:
-                        raise RuntimeError(f"armx_probe_read returned {st}")
-                for i in range(3):
-                    call(i)
-                for i, ev in enumerate(evs):
-                    call(i, ev)
-                torch.cuda.synchronize()
-                ms = sum(a.elapsed_time(b) for a, b in evs) / iters
-                results.append((2 * n / (ms * 1e-3) / 1e9, dict(
-                    block_threads=block, blocks=cus * per_cu, waves_per_cu=per_cu * block // 64,
-                    loads=loads, nontemporal=bool(nt), launch_ms_avg=ms)))
+        for loads, nt, pause in kinds:
+            def call(i, ev=(None, None)):
+                st = lib.armx_probe_read(bufs[i & 1].data_ptr(), n, out.data_ptr(), words,
+                                         cus * per_cu, block, loads, nt, pause,
+                                         ev[0].cuda_event if ev[0] else None,
+                                         ev[1].cuda_event if ev[1] else None, stream)
+                if st != 0:
+                    raise RuntimeError(f"armx_probe_read returned {st}")
+            for i in range(3):
+                call(i)
+            for i, ev in enumerate(evs):
+                call(i, ev)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in evs) / iters
+            results.append((2 * n / (ms * 1e-3) / 1e9, dict(
+                block_threads=block, blocks=cus * per_cu, waves_per_cu=per_cu * block // 64,
+                loads=loads, nontemporal=bool(nt), pause=pause, launch_ms_avg=ms)))
     results.sort(key=lambda r: -r[0])
     return results[0]
 

@@ -26,13 +26,15 @@ extern "C" {
  * A grid of `blocks` blocks of `block_threads` threads (a multiple of 64, at
  * most 1024); wavefront g of T takes steps g, g + T, ..., each step `loads`
  * consecutive 1 KiB wavefront loads (1, 2, 4, 8 or 16) issued back to back
- * and then consumed.  nontemporal != 0 uses non-temporal loads.
+ * and then consumed.  nontemporal != 0 uses non-temporal loads.  pause (0,
+ * 2, 4 or 8) makes each wavefront sleep about 64 * pause clocks after every
+ * step.
  * start_event / stop_event (hipEvent_t, may be NULL) are stamped by the
  * kernel's dispatch when it starts and completes.
  */
 int armx_probe_read(const void* x, size_t n, uint32_t* out, size_t out_words, int blocks,
-                    int block_threads, int loads, int nontemporal, void* start_event,
-                    void* stop_event, void* stream);
+                    int block_threads, int loads, int nontemporal, int pause,
+                    void* start_event, void* stop_event, void* stream);
 
 #ifdef __cplusplus
 }

@@ -221,13 +221,14 @@ def test_probe_library_exports_its_symbols_and_checks_arguments():
     assert names == ["armx_probe_read"]
     f = lib.armx_probe_read
     vp, sz, ci = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
-    f.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, vp, vp, vp]
+    f.argtypes = [vp, sz, vp, sz, ci, ci, ci, ci, ci, vp, vp, vp]
     f.restype = ci
     fake, words = 1 << 20, 1 << 20
-    assert f(None, 4096, fake, words, 1, 64, 8, 1, None, None, None) == -1
-    assert f(fake + 8, 4096, fake, words, 1, 64, 8, 1, None, None, None) == -2
-    assert f(fake, 4096, fake, words, 1, 96, 8, 1, None, None, None) == -3
-    assert f(fake, 4096, fake, words, 0, 64, 8, 1, None, None, None) == -3
-    assert f(fake, 4096, fake, words, 1, 64, 3, 1, None, None, None) == -3
-    assert f(fake, 4096 + 512, fake, words, 1, 64, 8, 1, None, None, None) == -5
-    assert f(fake, 4096, fake, 63, 1, 64, 8, 1, None, None, None) == -5
+    assert f(None, 4096, fake, words, 1, 64, 8, 1, 0, None, None, None) == -1
+    assert f(fake + 8, 4096, fake, words, 1, 64, 8, 1, 0, None, None, None) == -2
+    assert f(fake, 4096, fake, words, 1, 96, 8, 1, 0, None, None, None) == -3
+    assert f(fake, 4096, fake, words, 0, 64, 8, 1, 0, None, None, None) == -3
+    assert f(fake, 4096, fake, words, 1, 64, 3, 1, 0, None, None, None) == -3
+    assert f(fake, 4096 + 512, fake, words, 1, 64, 8, 1, 0, None, None, None) == -5
+    assert f(fake, 4096, fake, 63, 1, 64, 8, 1, 0, None, None, None) == -5
+    assert f(fake, 4096, fake, words, 1, 64, 8, 1, 3, None, None, None) == -3   # pause
