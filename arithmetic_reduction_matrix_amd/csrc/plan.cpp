@@ -69,12 +69,18 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 }
 
 // Automatic shapes for rows longer than one chunk (cols > 512), measured on
-// MI355X with 2^28 values.  Rows of fewer than 8 chunks carry a fixed cost
-// per row (the chain's result, the row combine, the store) that more
-// wavefronts hide: they take R = 1 (16 wavefronts per compute unit) and
-// blocks of 512 threads (8 consecutive rows per block); fixed-order rows of
-// exactly 2 or 4 chunks are one group each (R = chunks).  Longer rows keep
-// the per-operation defaults.
+// MI355X with 2^28 values.  A row stream keeps two chains in flight per
+// wavefront whatever they hold, so a row's last chain should be as full as
+// possible: one that holds a single chunk costs about as long as a full one
+// (9-chunk rows at R = 8: 172 us against 77 us at R = 3).
+//  * Rows of fewer than 8 chunks carry a fixed cost per row (the chain's
+//    result, the row combine, the store) that more wavefronts hide: R = 1
+//    (16 wavefronts per compute unit) in blocks of 512 threads; fixed-order
+//    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
+//    short fixed-order rows R = 1 in blocks of 256.
+//  * Longer rows: the R that pads the last chain least -- 4 to 8 for free
+//    order, 2 or 4 for fixed order (R = 2 only while a row stays within the
+//    flat kernel's 64 groups) -- the larger one on a tie, default blocks.
 struct RowShape {
   uint64_t r;
   int block;
@@ -82,9 +88,19 @@ struct RowShape {
 
 RowShape rows_auto_shape(uint64_t cols, const OpDefaults& d, bool fixed) {
   const uint64_t chunks = ceil_div(cols, kChunk);
-  if (chunks >= 8) return {uint64_t(d.r), d.block};
-  if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
-  return {1, fixed ? 256 : 512};
+  if (chunks < 8) {
+    if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
+    return {1, fixed ? 256 : 512};
+  }
+  auto waste = [&](uint64_t r) { return ceil_div(chunks, r) * r - chunks; };
+  if (fixed) {
+    const uint64_t r = (waste(2) < waste(4) && ceil_div(chunks, 2) <= 64) ? 2 : 4;
+    return {r, d.block};
+  }
+  uint64_t best = 8;
+  for (uint64_t r = 8; r >= 4; --r)
+    if (waste(r) < waste(best)) best = r;
+  return {best, d.block};
 }
 
 // Consecutive rows whose pitch is not a whole number of 128-byte lines share

@@ -57,6 +57,7 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   const uint64_t gpr = (cols + group_elems - 1) / group_elems;
   const bool partial = gpr * group_elems != cols;
   const uint64_t last_chunk = (cols - 1) / 512;
+  const u32x4* fill = neg_zero_chunk();
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * gpr;
   const uint64_t row_step = T * ld;
@@ -64,7 +65,7 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   uint64_t rk = 0, rc = 0;   // next (row, group) to reduce
   const uint16_t* load_row = x + g * ld;
   auto load = [&](u32x4 (&v)[R]) {
-    load_row_chain<R, NT>(load_row, lc, last_chunk, lane, v);
+    load_row_chain<R, NT>(load_row, lc, last_chunk, fill, lane, v);
     // stays on the last item once it is reached (the re-read is not used)
     const bool more_in_row = lc + 1 < gpr;
     const bool more_rows = lk + 1 < K;

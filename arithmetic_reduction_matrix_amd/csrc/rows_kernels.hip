@@ -53,13 +53,14 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
   const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
   const bool partial = cpr * chain_elems != cols;
   const uint64_t last_chunk = (cols - 1) / 512;
+  const u32x4* fill = neg_zero_chunk();
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * cpr;
   const uint64_t row_step = T * ld;
   RowCursor pf, rd, pr;   // next item to load, to reduce, to retire
   const uint16_t* load_row = x + g * ld;
   auto load = [&](u32x4 (&v)[R]) {
-    load_row_chain<R, NT>(load_row, pf.c, last_chunk, lane, v);
+    load_row_chain<R, NT>(load_row, pf.c, last_chunk, fill, lane, v);
     // stays on the last item once it is reached (the re-read is not used)
     if (pf.c + 1 < cpr) {
       ++pf.c;

@@ -111,8 +111,9 @@ typedef struct armx_config {
  * unit; chain_r has no effect there); rows of 513 to 3584 values take R = 1
  * and blocks of 512 threads (fixed order: R = 2 or 4 and 512 threads when a
  * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
- * rows the defaults above.  An explicit block_threads or chain_r overrides
- * its part. */
+ * rows the R that leaves a row's last chain of R chunks the least padding,
+ * 4 to 8 (fixed order: 2 or 4), with the default block size.  An explicit
+ * block_threads or chain_r overrides its part. */
 
 /*
  * reduce_sum -- out[0] = sum of x[0..n), free summation order.
