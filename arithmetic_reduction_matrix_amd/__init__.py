@@ -16,7 +16,8 @@ Entry points (same names as the C ABI):
 * ``reduce_rows(x)`` -- float32 sum of every row of a 2-D float16 tensor.
 * ``reduce_sum_fixed_order(x)`` -- sum in one prescribed balanced-tree order,
   bit-identical for every configuration ("Taming Bitwise Behavior in GPU
-  Kernels with Tensor Core", arXiv 2609.11356, Abstract).
+  Kernels with Tensor Core", arXiv 2609.11356, Abstract); ``mma_leaves=True``
+  selects the prescribed order whose leaves are MFMAs.
 * ``reduce_rows_fixed_order(x)`` -- the same order per row: each row's bits
   depend on that row only (batch invariance, same Abstract).
 * ``reduce_sum_exact(x)`` -- the correctly rounded float32 of the exact sum
@@ -36,6 +37,7 @@ __all__ = [
     "reduce_sum_exact", "fixed_to_int", "workspace_bytes", "ArmxError", "Config", "LIB_PATH",
     "OP_SUM", "OP_ROWS", "OP_FIXED", "OP_ROWS_FIXED", "OP_EXACT",
     "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS", "FLAG_MMA_LEVELS",
+    "FLAG_MMA_LEAVES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so")
@@ -43,6 +45,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so"
 OP_SUM, OP_ROWS, OP_FIXED, OP_ROWS_FIXED, OP_EXACT = 0, 1, 2, 3, 4
 FLAG_PLAIN, FLAG_CACHED_LOADS, FLAG_ONE_CHAIN, FLAG_TWO_PASS = 0x1, 0x2, 0x4, 0x8
 FLAG_MMA_LEVELS = 0x10
+FLAG_MMA_LEAVES = 0x20
 
 _STATUS = {
     0: "ARMX_OK", -1: "ARMX_ERR_NULL", -2: "ARMX_ERR_ALIGN", -3: "ARMX_ERR_CONFIG",
@@ -104,11 +107,11 @@ def _event_handle(ev) -> int | None:
 
 
 def _config(block_threads=0, chain_r=0, grid_blocks=0, plain=False, cached_loads=False,
-            one_chain=False, two_pass=False, mma_levels=False, start_event=None,
-            stop_event=None) -> Config:
+            one_chain=False, two_pass=False, mma_levels=False, mma_leaves=False,
+            start_event=None, stop_event=None) -> Config:
     flags = ((FLAG_PLAIN if plain else 0) | (FLAG_CACHED_LOADS if cached_loads else 0)
              | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0)
-             | (FLAG_MMA_LEVELS if mma_levels else 0))
+             | (FLAG_MMA_LEVELS if mma_levels else 0) | (FLAG_MMA_LEAVES if mma_leaves else 0))
     return Config(int(block_threads), int(chain_r), int(grid_blocks), flags,
                   _event_handle(start_event), _event_handle(stop_event))
 

@@ -40,7 +40,7 @@ namespace {
 using namespace dev;
 using namespace dev::tree;
 
-template <int R, bool NT>
+template <int R, bool NT, bool MMA>
 __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x, uint64_t n,
                                                      int log2c, unsigned slots_per_wave,
                                                      unsigned* __restrict__ counters,
@@ -64,8 +64,8 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
   float* log_rows = node_lds + unsigned(wave_id()) * slots_per_wave;
   const float wave_root =
       valid / R >= kPaceLongChains
-          ? wave_range_root<R, NT, 2>(x, n, first, valid, lane, log_rows)
-          : wave_range_root<R, NT>(x, n, first, valid, lane, log_rows);
+          ? wave_range_root<R, NT, 2, MMA>(x, n, first, valid, lane, log_rows)
+          : wave_range_root<R, NT, 0, MMA>(x, n, first, valid, lane, log_rows);
 
   // block: W consecutive wavefront subtrees -> one subtree
   __syncthreads();
@@ -101,21 +101,24 @@ __global__ __launch_bounds__(1024) void fixed_final_kernel(const float* __restri
 }
 
 template <int R>
-const void* pick_fixed(bool nt) {
-  return nt ? reinterpret_cast<const void*>(&fixed_kernel<R, true>)
-            : reinterpret_cast<const void*>(&fixed_kernel<R, false>);
+const void* pick_fixed(bool nt, bool mma) {
+  if (mma)
+    return nt ? reinterpret_cast<const void*>(&fixed_kernel<R, true, true>)
+              : reinterpret_cast<const void*>(&fixed_kernel<R, false, true>);
+  return nt ? reinterpret_cast<const void*>(&fixed_kernel<R, true, false>)
+            : reinterpret_cast<const void*>(&fixed_kernel<R, false, false>);
 }
 
-const void* fixed_kernel_for(int r, bool nt) {
+const void* fixed_kernel_for(int r, bool nt, bool mma) {
   switch (r) {
-    case 1: return pick_fixed<1>(nt);
-    case 2: return pick_fixed<2>(nt);
-    case 3: return pick_fixed<3>(nt);
-    case 4: return pick_fixed<4>(nt);
-    case 5: return pick_fixed<5>(nt);
-    case 6: return pick_fixed<6>(nt);
-    case 7: return pick_fixed<7>(nt);
-    case 8: return pick_fixed<8>(nt);
+    case 1: return pick_fixed<1>(nt, mma);
+    case 2: return pick_fixed<2>(nt, mma);
+    case 3: return pick_fixed<3>(nt, mma);
+    case 4: return pick_fixed<4>(nt, mma);
+    case 5: return pick_fixed<5>(nt, mma);
+    case 6: return pick_fixed<6>(nt, mma);
+    case 7: return pick_fixed<7>(nt, mma);
+    case 8: return pick_fixed<8>(nt, mma);
     default: return nullptr;
   }
 }
@@ -125,7 +128,8 @@ const void* fixed_kernel_for(int r, bool nt) {
 hipError_t launch_fixed(const Plan& plan, const void* x, float* out, void* ws,
                         hipStream_t stream) {
   if (plan.n == 0) return launch_zero(out, 1, stream);
-  const void* fn = fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  const void* fn = fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                    (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
   if (!fn) return hipErrorInvalidValue;
   const u32x4* xv = static_cast<const u32x4*>(x);
   uint64_t n = plan.n;

@@ -45,6 +45,17 @@ __device__ __forceinline__ float chunk_node(u32x4 t) {
   return add_xor32(add_xor16(chunk_rows(t)));
 }
 
+// Node of one chunk in the order with MFMA leaves: one
+// v_mfma_f32_16x16x32_f16 of the chunk against all-ones from a zero
+// accumulator gives the 16 column sums (lane l holds column l % 16, and the
+// four 16-lane rows hold the same values), then the balanced tree over the 16
+// columns in column order (levels xor 1, xor 2, the mirror in 8 and the
+// mirror in 16), so every lane ends with the chunk node.
+__device__ __forceinline__ float chunk_node_mma(u32x4 t) {
+  const floatx4 cols = mfma_ones(floatx4{0.0f, 0.0f, 0.0f, 0.0f}, t);
+  return lane_tree(cols[0], 4);
+}
+
 // Node of a power-of-two group of R consecutive chunks (an aligned subtree of
 // 512 R values), identical in every lane.  After levels 1-7 each chunk is four
 // row nodes [c0 c1 c2 c3]; the remaining levels pair rows, halves and then
@@ -203,9 +214,26 @@ struct NodeLog {
 // Reduces R loaded chunks (items k0 .. k0 + R - 1, k0 a multiple of R) and
 // records their node(s): the group's subtree root for R = 2, 4, 8, else one
 // node per chunk.  Straight-line code; nothing here branches.
-template <int R>
+// With MMA (the order with MFMA leaves) the chunk nodes come from
+// chunk_node_mma and a power-of-two group adds them pairwise in index order.
+template <int R, bool MMA = false>
 __device__ __forceinline__ void reduce_group(const u32x4 (&v)[R], NodeLog& log, int lane) {
-  if constexpr (R == 1) {
+  if constexpr (MMA) {
+    float node[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) node[r] = chunk_node_mma(v[r]);
+    if constexpr (is_pow2(R)) {
+#pragma unroll
+      for (int s = 1; s < R; s *= 2) {
+#pragma unroll
+        for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
+      }
+      log.record(node[0], lane);
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) log.record(node[r], lane);
+    }
+  } else if constexpr (R == 1) {
     log.record(chunk_node(v[0]), lane);
   } else if constexpr (is_pow2(R)) {
     log.record(group_node<R>(v), lane);
@@ -244,7 +272,7 @@ __device__ inline float wave_tree(float* vals, unsigned count, int lane) {
 // array x (leaves past n read as -0.0), by one wavefront (every lane returns
 // it); the range must be the valid prefix of an aligned power-of-two range.
 // `log_rows` is this wavefront's LDS node log.
-template <int R, bool NT, int PACE = 0>
+template <int R, bool NT, int PACE = 0, bool MMA = false>
 __device__ __forceinline__ float wave_range_root(const u32x4* __restrict__ x, uint64_t n,
                                                  uint64_t first, uint64_t valid, int lane,
                                                  float* log_rows) {
@@ -266,15 +294,15 @@ __device__ __forceinline__ float wave_range_root(const u32x4* __restrict__ x, ui
     for (; g + 1 < groups; g += 2) {
       load_group<R, NT>(x, first + (g + 1) * R, lane, b);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
-      reduce_group<R>(a, log, lane);
+      reduce_group<R, MMA>(a, log, lane);
       pace_pause<PACE>();
       load_group<R, NT>(x, first + (g + 2 < groups ? g + 2 : g + 1) * R, lane, a);
       __builtin_amdgcn_sched_barrier(0);
-      reduce_group<R>(b, log, lane);
+      reduce_group<R, MMA>(b, log, lane);
       pace_pause<PACE>();
     }
     if (g < groups) {
-      reduce_group<R>(a, log, lane);
+      reduce_group<R, MMA>(a, log, lane);
       ++g;
     }
   }
@@ -292,7 +320,11 @@ __device__ __forceinline__ float wave_range_root(const u32x4* __restrict__ x, ui
         const u32x4 v = gk < full ? load16<NT>(x + gk * 64 + lane)
                                   : load8_masked(reinterpret_cast<const uint16_t*>(x),
                                                  gk * 512 + uint64_t(lane) * 8, n, 0x8000u);
-        node[r] = chunk_node(v);
+        if constexpr (MMA) {
+          node[r] = chunk_node_mma(v);
+        } else {
+          node[r] = chunk_node(v);
+        }
       }
     }
     if constexpr (is_pow2(R)) {

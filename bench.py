@@ -322,6 +322,11 @@ def main() -> int:
         fixed_val = armx.reduce_sum_fixed_order(fbufs[0]).cpu().numpy()
         var["fixed_order_2p26"] = {"ms": ms, "gbs": 2 * xf_np.size / ms / 1e6,
                                    "result_bits": int(fixed_val.view(np.uint32))}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum_fixed_order(
+            fbufs[i & 3], mma_leaves=True), 200)
+        mma_val = armx.reduce_sum_fixed_order(fbufs[0], mma_leaves=True).cpu().numpy()
+        var["fixed_order_mma_leaves_2p26"] = {"ms": ms, "gbs": 2 * xf_np.size / ms / 1e6,
+                                              "result_bits": int(mma_val.view(np.uint32))}
         del fbufs
 
         xr_np = si.workload("rows_4096x65536_normal")

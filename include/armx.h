@@ -82,6 +82,8 @@ typedef enum armx_status {
 #define ARMX_FLAG_MMA_LEVELS 0x10u /* reduce_sum: the recursive all-MMA form   */
                                    /* (see reduce_sum); not with PLAIN or      */
                                    /* TWO_PASS                                 */
+#define ARMX_FLAG_MMA_LEAVES 0x20u /* reduce_sum_fixed_order: the fixed order  */
+                                   /* whose leaves are MFMAs (see there)       */
 
 typedef struct armx_config {
   int block_threads; /* 0 = default; else 64..1024, a multiple of 64.         */
@@ -194,6 +196,17 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out,
  * complete subtree.  The result is bit-identical for every block size,
  * chain length, grid and device, and n == 0 gives +0.0.  Only binary32
  * additions are used (no MFMA and no fused multiply-add).
+ *
+ * With ARMX_FLAG_MMA_LEAVES the prescribed order has tensor-core leaves (the
+ * same Abstract reconstructs tensor-core arithmetic from outputs; this
+ * library's reconstruction of the gfx950 MFMA is what makes such an order
+ * checkable): x is cut into chunks of 512 values (the last padded with
+ * -0.0), each chunk is one v_mfma_f32_16x16x32_f16 against all-ones from a
+ * zero accumulator -- column j sums, in K order, values 8s .. 8s + 7 of the
+ * slots s = j, j + 16, j + 32, j + 48 -- and the chunk's node is the balanced
+ * tree over its 16 column sums in column order; above the chunks the
+ * balanced tree as before.  It too is bit-identical for every block size,
+ * chain length, grid and device.
  *
  * x, n, out, ws, ws_bytes as for reduce_sum.  block_threads must be a power
  * of two.  ARMX_FLAG_PLAIN and ARMX_FLAG_ONE_CHAIN are not accepted.

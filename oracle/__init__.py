@@ -26,19 +26,28 @@ What it computes:
 * ``fixed_tree_sum`` / ``fixed_tree_row_sums`` -- the prescribed fixed order:
   a balanced binary tree over the inputs (padded to a power of two with -0.0),
   every node one binary32 round-to-nearest-even addition.
+* ``fixed_tree_sum_mma_leaves`` -- the prescribed order with MFMA leaves:
+  chunks of 512 values, each one MFMA against ones from zero as reconstructed
+  in ``mfma_model`` (16 column sums, then their balanced tree), and the
+  balanced tree over the chunks.
+* ``mfma_model`` -- the reconstructed accumulation of the gfx950 MFMA (a
+  description of hardware behaviour fitted to black-box probes; its header
+  says which parts the pages do not pin).
 
 Every function is pinned by tests under ``tests/`` to something other than
 itself (library routines, brute force with rationals, closed forms, worked
-examples and invariants); none is "parity unpinned".
+examples and invariants).  The MFMA model and the MFMA-leaf order built on it
+describe hardware the pages do not describe: parity unpinned against the
+pages, pinned to the model's own definition and to closed forms.
 """
 from .binary16 import decode_table, decode_bits, BINARY16_QUANTUM_EXP
 from .rounding import round_scaled_int, to_binary32, to_binary64
 from .exact import ExactSum, exact_sum, exact_row_sums
-from .tree import fixed_tree_sum, fixed_tree_row_sums
+from .tree import fixed_tree_sum, fixed_tree_row_sums, fixed_tree_sum_mma_leaves
 
 __all__ = [
     "decode_table", "decode_bits", "BINARY16_QUANTUM_EXP",
     "round_scaled_int", "to_binary32", "to_binary64",
     "ExactSum", "exact_sum", "exact_row_sums",
-    "fixed_tree_sum", "fixed_tree_row_sums",
+    "fixed_tree_sum", "fixed_tree_row_sums", "fixed_tree_sum_mma_leaves",
 ]

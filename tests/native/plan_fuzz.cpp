@@ -82,7 +82,7 @@ int main(int argc, char** argv) {
     if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
     c.chain_r = int(rng() % 10);
     c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
-    c.flags = unsigned(rng() % 32);
+    c.flags = unsigned(rng() % 64);
     const uint64_t n = pick_n();
     const uint64_t cols = pick_n() % (uint64_t(1) << 30);
     const uint64_t ld = (rng() % 2) ? cols : cols + (rng() % 64);
@@ -99,6 +99,8 @@ int main(int argc, char** argv) {
     const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
     EXPECT(W >= 1 && W <= 16 && R >= 1 && R <= 8, "W %llu R %llu", (unsigned long long)W,
            (unsigned long long)R);
+    EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || op == ARMX_OP_FIXED,
+           "MMA leaves accepted for op %d", op);
     const bool levels = (p.flags & ARMX_FLAG_MMA_LEVELS) != 0;
     EXPECT(!levels || op == ARMX_OP_SUM, "levels flag accepted for op %d", op);
     if (levels) {

@@ -127,6 +127,19 @@ def test_mma_levels_config_rules():
     assert f(FAKE, 1 << 20, FAKE, ws, 256, cfg(mma_levels=True), None) == -4
 
 
+def test_mma_leaves_config_rules():
+    # the MFMA-leaf order belongs to reduce_sum_fixed_order only
+    ws = 1 << 24
+    assert armx.lib.reduce_sum(FAKE, 10, FAKE, ws, 1 << 20, cfg(mma_leaves=True), None) == -3
+    assert armx.lib.reduce_sum_exact(FAKE, 10, FAKE, None, ws, 1 << 20, cfg(mma_leaves=True),
+                                     None) == -3
+    assert armx.lib.reduce_rows(FAKE, 4, 96, 96, FAKE, None, 0, cfg(mma_leaves=True), None) == -3
+    assert armx.lib.reduce_rows_fixed_order(FAKE, 4, 96, 96, FAKE, None, 0, cfg(mma_leaves=True),
+                                            None) == -3
+    assert armx.workspace_bytes(armx.OP_FIXED, 1 << 20, mma_leaves=True) == \
+        armx.workspace_bytes(armx.OP_FIXED, 1 << 20)
+
+
 def test_mma_levels_workspace_sizes():
     # counter region + level-1 values + level-2 values, each rounded to 256 B;
     # nothing when level 1 gives one value (n <= 512 R)
