@@ -7,8 +7,8 @@
 // accumulators.  A chunk never straddles two rows: the chunk grid restarts
 // at every row (rows are 16-byte aligned because ld is a multiple of 8), and
 // a row's last partial chain is masked.  Rows of at most 512 values go to
-// the segmented kernel of short_rows_kernels.hip instead.  The row's fp32 total is written
-// directly -- no workspace, no second pass.  Two mappings:
+// the segmented kernel of short_rows_kernels.hip instead.  The row's fp32
+// total is written directly -- no workspace, no second pass.  Two mappings:
 //  * wave_rows: each wavefront sums whole rows (rows g, g + T, ... for
 //    wavefront g of T); the loads of the next row are issued before the
 //    current row is finished, so the pipeline runs across rows, and a row's
