@@ -19,7 +19,8 @@ Entry points (same names as the C ABI):
   Kernels with Tensor Core", arXiv 2609.11356, Abstract); ``mma_leaves=True``
   selects the prescribed order whose leaves are MFMAs.
 * ``reduce_rows_fixed_order(x)`` -- the same order per row: each row's bits
-  depend on that row only (batch invariance, same Abstract).
+  depend on that row only (batch invariance, same Abstract); ``mma_leaves``
+  as above.
 * ``reduce_sum_exact(x)`` -- the correctly rounded float32 of the exact sum
   (and, with ``fixed=``, the exact sum as a 128-bit count of 2^-24), the
   same bits for every configuration.
@@ -284,6 +285,7 @@ def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> t
 def reduce_rows_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
                             **cfg) -> torch.Tensor:
     """Balanced-tree-order float32 sum of every row (as reduce_rows): row r's
-    bits depend on row r's values only (batch invariant)."""
+    bits depend on row r's values only (batch invariant).  ``mma_leaves=True``
+    gives each row the order with MFMA leaves of reduce_sum_fixed_order."""
     return _rows_call(lib.reduce_rows_fixed_order, x, out, _config(**cfg),
                       "reduce_rows_fixed_order")

@@ -20,6 +20,8 @@ namespace tree {
 
 constexpr int kStack = kFixedMaxLog2Chunks + 1;
 
+constexpr bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
 // Level 1 of the tree for the two binary16 values in one 32-bit word:
 // fl32(lo + hi).  v_fma_mix_f32 takes both halves as f16 operands (op_sel)
 // and computes lo * 1.0 + hi with one round-to-nearest-even rounding; the
@@ -54,6 +56,22 @@ __device__ __forceinline__ float chunk_node(u32x4 t) {
 __device__ __forceinline__ float chunk_node_mma(u32x4 t) {
   const floatx4 cols = mfma_ones(floatx4{0.0f, 0.0f, 0.0f, 0.0f}, t);
   return lane_tree(cols[0], 4);
+}
+
+// Node of a power-of-two group of R consecutive chunks in the order with
+// MFMA leaves: the chunk nodes added pairwise in index order.
+template <int R>
+__device__ __forceinline__ float group_node_mma(const u32x4 (&v)[R]) {
+  static_assert(is_pow2(R), "a group subtree needs a power-of-two R");
+  float node[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) node[r] = chunk_node_mma(v[r]);
+#pragma unroll
+  for (int s = 1; s < R; s *= 2) {
+#pragma unroll
+    for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
+  }
+  return node[0];
 }
 
 // Node of a power-of-two group of R consecutive chunks (an aligned subtree of
@@ -185,8 +203,6 @@ __device__ __forceinline__ void load_group(const u32x4* __restrict__ x, uint64_t
   for (int r = 0; r < R; ++r) v[r] = load16<NT>(p + r * 64);
 }
 
-constexpr bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
-
 // Nodes recorded per group of R chunks: one (the group's subtree root) when R
 // is a power of two -- then a group of R consecutive, R-aligned chunks is a
 // complete subtree -- else one per chunk.
@@ -219,17 +235,12 @@ struct NodeLog {
 template <int R, bool MMA = false>
 __device__ __forceinline__ void reduce_group(const u32x4 (&v)[R], NodeLog& log, int lane) {
   if constexpr (MMA) {
-    float node[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) node[r] = chunk_node_mma(v[r]);
     if constexpr (is_pow2(R)) {
-#pragma unroll
-      for (int s = 1; s < R; s *= 2) {
-#pragma unroll
-        for (int i = 0; i < R; i += 2 * s) node[i] = node[i] + node[i + s];
-      }
-      log.record(node[0], lane);
+      log.record(group_node_mma<R>(v), lane);
     } else {
+      float node[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) node[r] = chunk_node_mma(v[r]);
 #pragma unroll
       for (int r = 0; r < R; ++r) log.record(node[r], lane);
     }

@@ -166,7 +166,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   uint64_t R = uint64_t(p.r);
 
   if (op != kOpSum && (c.flags & ARMX_FLAG_MMA_LEVELS)) return ARMX_ERR_CONFIG;
-  if (op != kOpFixed && (c.flags & ARMX_FLAG_MMA_LEAVES)) return ARMX_ERR_CONFIG;
+  if (op != kOpFixed && op != kOpRowsFixed && (c.flags & ARMX_FLAG_MMA_LEAVES))
+    return ARMX_ERR_CONFIG;
   if (op == kOpExact) {
     // persistent grid as for the free-order sum; only the load kind is a flag
     if (c.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS)) return ARMX_ERR_CONFIG;

@@ -28,6 +28,13 @@
 //    of two) take aligned power-of-two chunk ranges of the row and reduce
 //    them as the flat fixed-order kernel does; the W roots are combined by a
 //    lane tree.
+// MMA selects the order with MFMA leaves (every chunk node one
+// v_mfma_f32_16x16x32_f16 against ones and the tree over its 16 column sums,
+// as for the flat fixed-order sum), per row.  A chunk that lies wholly past
+// the row (the -0.0 reads of a partial last group) then has node +0.0 instead
+// of -0.0: an MFMA from a zero accumulator never returns -0.0, so no node of
+// the row's own chunks is -0.0, and adding +0.0 to such a node leaves it as it
+// is, exactly as -0.0 would.
 #include "fixed_tree.hpp"
 #include "launch.h"
 
@@ -38,16 +45,18 @@ using namespace dev;
 using namespace dev::tree;
 
 // Root of one loaded group (R chunks, R-aligned, R a power of two).
-template <int R>
+template <int R, bool MMA>
 __device__ __forceinline__ float group_root(const u32x4 (&v)[R]) {
-  if constexpr (R == 1) {
+  if constexpr (MMA) {
+    return group_node_mma<R>(v);
+  } else if constexpr (R == 1) {
     return chunk_node(v[0]);
   } else {
     return group_node<R>(v);
   }
 }
 
-template <int R, bool NT>
+template <int R, bool NT, bool MMA>
 __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                                 uint64_t cols, uint64_t ld,
                                                 float* __restrict__ out, uint64_t g, uint64_t T,
@@ -76,7 +85,7 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   float slots = -0.0f;
   auto reduce = [&](u32x4 (&v)[R]) {
     if (partial && rc + 1 == gpr) mask_row_chain<R>(v, rc, cols, 0x8000u, lane);
-    const float node = group_root<R>(v);
+    const float node = group_root<R, MMA>(v);
     slots = uint64_t(lane) == rc ? node : (rc == 0 ? -0.0f : slots);
     const float root = lane_tree_full(slots);
     out[g + rk * T] = root;  // every group; the row's last group writes the root
@@ -102,7 +111,7 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
 // past the row: the same group subtrees and slot register as rows_fixed_flat,
 // its whole groups streamed with the same ping-pong pipeline, the partial last
 // group read with exact masked loads.
-template <int R, bool NT>
+template <int R, bool NT, bool MMA>
 __device__ __forceinline__ float row_root_masked(const uint16_t* __restrict__ xr, uint64_t cols,
                                                  int lane) {
   const uint64_t group_elems = uint64_t(R) * 512;
@@ -111,7 +120,7 @@ __device__ __forceinline__ float row_root_masked(const uint16_t* __restrict__ xr
   const u32x4* x4 = reinterpret_cast<const u32x4*>(xr);
   float slots = -0.0f;
   auto take = [&](uint64_t gi, const u32x4 (&v)[R]) {
-    const float node = group_root<R>(v);
+    const float node = group_root<R, MMA>(v);
     slots = uint64_t(lane) == gi ? node : slots;
   };
   uint64_t gi = 0;
@@ -141,7 +150,7 @@ __device__ __forceinline__ float row_root_masked(const uint16_t* __restrict__ xr
   return lane_tree_full(slots);
 }
 
-template <int R, bool NT>
+template <int R, bool NT, bool MMA>
 __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __restrict__ x,
                                                           uint64_t rows, uint64_t cols,
                                                           uint64_t ld, float* __restrict__ out,
@@ -157,9 +166,9 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
       const uint64_t T = uint64_t(gridDim.x) * W;
       // the last row stays out of the stream when rows end inside a group
       const bool tail = cols % (uint64_t(R) * 512) != 0;
-      rows_fixed_flat<R, NT>(x, tail ? rows - 1 : rows, cols, ld, out, g, T, lane);
+      rows_fixed_flat<R, NT, MMA>(x, tail ? rows - 1 : rows, cols, ld, out, g, T, lane);
       if (tail && g == (rows - 1) % T) {
-        const float root = row_root_masked<R, NT>(x + (rows - 1) * ld, cols, lane);
+        const float root = row_root_masked<R, NT, MMA>(x + (rows - 1) * ld, cols, lane);
         if (lane == 0) out[rows - 1] = root;
       }
     }
@@ -176,7 +185,8 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
   while ((1 << lv) < W) ++lv;
   for (uint64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * ld);
-    const float wave_root = wave_range_root<R, NT>(xr, cols, first, valid, lane, log_rows);
+    const float wave_root =
+        wave_range_root<R, NT, 0, MMA>(xr, cols, first, valid, lane, log_rows);
     __syncthreads();
     if (lane == 0) red[wave_id()] = wave_root;
     __syncthreads();
@@ -188,21 +198,24 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
 }
 
 template <int R>
-const void* pick_rows_fixed(bool nt) {
-  return nt ? reinterpret_cast<const void*>(&rows_fixed_kernel<R, true>)
-            : reinterpret_cast<const void*>(&rows_fixed_kernel<R, false>);
+const void* pick_rows_fixed(bool nt, bool mma) {
+  if (mma)
+    return nt ? reinterpret_cast<const void*>(&rows_fixed_kernel<R, true, true>)
+              : reinterpret_cast<const void*>(&rows_fixed_kernel<R, false, true>);
+  return nt ? reinterpret_cast<const void*>(&rows_fixed_kernel<R, true, false>)
+            : reinterpret_cast<const void*>(&rows_fixed_kernel<R, false, false>);
 }
 
-const void* rows_fixed_kernel_for(int r, bool nt) {
+const void* rows_fixed_kernel_for(int r, bool nt, bool mma) {
   switch (r) {
-    case 1: return pick_rows_fixed<1>(nt);
-    case 2: return pick_rows_fixed<2>(nt);
-    case 3: return pick_rows_fixed<3>(nt);
-    case 4: return pick_rows_fixed<4>(nt);
-    case 5: return pick_rows_fixed<5>(nt);
-    case 6: return pick_rows_fixed<6>(nt);
-    case 7: return pick_rows_fixed<7>(nt);
-    case 8: return pick_rows_fixed<8>(nt);
+    case 1: return pick_rows_fixed<1>(nt, mma);
+    case 2: return pick_rows_fixed<2>(nt, mma);
+    case 3: return pick_rows_fixed<3>(nt, mma);
+    case 4: return pick_rows_fixed<4>(nt, mma);
+    case 5: return pick_rows_fixed<5>(nt, mma);
+    case 6: return pick_rows_fixed<6>(nt, mma);
+    case 7: return pick_rows_fixed<7>(nt, mma);
+    case 8: return pick_rows_fixed<8>(nt, mma);
     default: return nullptr;
   }
 }
@@ -213,7 +226,8 @@ hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStr
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
   if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
-  const void* fn = rows_fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  const void* fn = rows_fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                         (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
   if (!fn) return hipErrorInvalidValue;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;

@@ -16,7 +16,15 @@
 // root.  The result is the row's fixed-order sum, which is also a valid
 // free-order sum: the all-ones MFMA of "GPU Tensor Cores for fast Arithmetic
 // Reductions" (arXiv 2001.05585, Abstract) adds values of lanes 16 apart,
-// which here belong to different rows, so it is not used for these rows.
+// which here belong to different rows, so one MFMA per load cannot serve.
+//
+// With MMA (the order with MFMA leaves, for the fixed-order entry point) a
+// row's node is instead the one its 512-value chunk has in that order: one
+// v_mfma_f32_16x16x32_f16 against ones from a zero accumulator, column j
+// summing the row's slots j, j + 16, j + 32, j + 48 in that K order, and the
+// balanced tree over the 16 column sums.  Since lanes 16 apart feed the same
+// MFMA column, every block of max(16, P) lanes gets an MFMA of its own with
+// the other lanes' values zeroed (short_row_node_mma).
 //
 // The loop body has no branches.  Every load is unconditional: a lane past
 // the row's last slot reads the last slot again, a row past the end reads the
@@ -45,7 +53,46 @@ __device__ __forceinline__ float leaf8(u32x4 t) {
   return b0 + b1;
 }
 
-template <int S, bool NT>
+// A row's node in the order with MFMA leaves, for rows of P = 2^S lanes
+// packed 64 / P to a load (lane i of a row is its slot i).  Lane blocks of
+// 2^B = max(16, P) lanes each take one MFMA against ones from a zero
+// accumulator, with every lane outside the block zeroed.  The K positions of
+// such an MFMA that hold zeros leave the zero accumulator as it is, and the
+// block's slots sit in K order (slot i of a P = 32 row in the upper half at K
+// group 2 + i / 16), so each column sum is the one the row's own chunk gives.
+// Lane l then holds column l % 16 of its block: its own column.  The tree over
+// the row's 16 columns follows: for P < 16 the columns past the row's slots
+// are +0.0 sums and form subtrees of +0.0, which leave a node that is not
+// -0.0 unchanged (no MFMA from a zero accumulator returns -0.0), so the tree
+// over the row's P lanes is the node; for P = 32 the two 16-lane halves hold
+// the same columns and each finishes the tree alone.
+template <int S>
+__device__ __forceinline__ float short_row_node_mma(u32x4 t, int lane) {
+  constexpr int B = S < 4 ? 4 : S;
+  constexpr int NB = 64 >> B;
+  const int blk = lane >> B;
+  float own = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    u32x4 tq;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) tq[w] = blk == q ? t[w] : 0u;
+    const float c = mfma_ones(floatx4{0.0f, 0.0f, 0.0f, 0.0f}, tq)[0];
+    own = blk == q ? c : own;
+  }
+  return lane_tree(own, S < 4 ? S : 4);
+}
+
+template <int S, bool MMA>
+__device__ __forceinline__ float short_row_node(u32x4 t, int lane) {
+  if constexpr (MMA) {
+    return short_row_node_mma<S>(t, lane);
+  } else {
+    return lane_tree(leaf8(t), S);
+  }
+}
+
+template <int S, bool NT, bool MMA>
 __global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __restrict__ x,
                                                           uint64_t rows, uint64_t cols,
                                                           uint64_t ld, float* __restrict__ out,
@@ -75,7 +122,7 @@ __global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __rest
   const uint64_t body = ragged ? rows - 1 : rows;   // rows read with whole slots
   if (ragged && g == T - 1) {
     const uint16_t* xr = x + (rows - 1) * ld;
-    const float root = lane_tree(leaf8(load8_clamped(xr, e, cols, 0x8000u)), S);
+    const float root = short_row_node<S, MMA>(load8_clamped(xr, e, cols, 0x8000u), lane);
     if (lane == 0) out[rows - 1] = root;
   }
 
@@ -97,7 +144,7 @@ __global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __rest
       u32x4 t;
 #pragma unroll
       for (int w = 0; w < 4; ++w) t[w] = (v[u][w] & keep[w]) | (kNegZero2 & ~keep[w]);
-      out[row_of(c, u)] = lane_tree(leaf8(t), S);   // every lane of the row: the same value
+      out[row_of(c, u)] = short_row_node<S, MMA>(t, lane);   // the same in every lane of the row
     }
   };
   auto step = [&](uint64_t j) { return g + (j < K ? j : K - 1) * T; };
@@ -118,20 +165,23 @@ __global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __rest
 }
 
 template <int S>
-const void* pick_short(bool nt) {
-  return nt ? reinterpret_cast<const void*>(&short_rows_kernel<S, true>)
-            : reinterpret_cast<const void*>(&short_rows_kernel<S, false>);
+const void* pick_short(bool nt, bool mma) {
+  if (mma)
+    return nt ? reinterpret_cast<const void*>(&short_rows_kernel<S, true, true>)
+              : reinterpret_cast<const void*>(&short_rows_kernel<S, false, true>);
+  return nt ? reinterpret_cast<const void*>(&short_rows_kernel<S, true, false>)
+            : reinterpret_cast<const void*>(&short_rows_kernel<S, false, false>);
 }
 
-const void* short_rows_kernel_for(int s, bool nt) {
+const void* short_rows_kernel_for(int s, bool nt, bool mma) {
   switch (s) {
-    case 0: return pick_short<0>(nt);
-    case 1: return pick_short<1>(nt);
-    case 2: return pick_short<2>(nt);
-    case 3: return pick_short<3>(nt);
-    case 4: return pick_short<4>(nt);
-    case 5: return pick_short<5>(nt);
-    case 6: return pick_short<6>(nt);
+    case 0: return pick_short<0>(nt, mma);
+    case 1: return pick_short<1>(nt, mma);
+    case 2: return pick_short<2>(nt, mma);
+    case 3: return pick_short<3>(nt, mma);
+    case 4: return pick_short<4>(nt, mma);
+    case 5: return pick_short<5>(nt, mma);
+    case 6: return pick_short<6>(nt, mma);
     default: return nullptr;
   }
 }
@@ -141,7 +191,8 @@ const void* short_rows_kernel_for(int s, bool nt) {
 hipError_t launch_short_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0 || plan.n > kChunk) return hipErrorInvalidValue;
-  const void* fn = short_rows_kernel_for(plan.seg_log2, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  const void* fn = short_rows_kernel_for(plan.seg_log2, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                         (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
   if (!fn) return hipErrorInvalidValue;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;

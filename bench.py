@@ -28,6 +28,7 @@ Reductions" (arXiv 2001.05585, Abstract), which counts levels.
 from __future__ import annotations
 
 import argparse
+import functools
 import hashlib
 import json
 import os
@@ -341,6 +342,10 @@ def main() -> int:
         ms, med = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(rbufs[i & 1],
                                                                              out=rout), 200)
         var["rows_fixed_order_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
+        ms, med = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(
+            rbufs[i & 1], out=rout, mma_leaves=True), 200)
+        var["rows_fixed_order_mma_leaves_4096x65536"] = {"ms": ms,
+                                                         "gbs": 2 * xr_np.size / ms / 1e6}
         del rbufs
         # short and ragged rows: the headline buffers viewed as matrices;
         # bytes counted are the reads plus the fp32 results
@@ -349,7 +354,10 @@ def main() -> int:
             views = [b[: nrows * cols].view(nrows, cols) for b in bufs]
             vout = torch.empty(nrows, dtype=torch.float32, device=dev)
             moved = 2 * nrows * cols + 4 * nrows
-            for tag, fn in (("rows", armx.reduce_rows), ("rows_fixed_order", armx.reduce_rows_fixed_order)):
+            mma_rows = functools.partial(armx.reduce_rows_fixed_order, mma_leaves=True)
+            for tag, fn in (("rows", armx.reduce_rows),
+                            ("rows_fixed_order", armx.reduce_rows_fixed_order),
+                            ("rows_fixed_order_mma_leaves", mma_rows)):
                 ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
                 var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
             del views, vout

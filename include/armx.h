@@ -82,8 +82,9 @@ typedef enum armx_status {
 #define ARMX_FLAG_MMA_LEVELS 0x10u /* reduce_sum: the recursive all-MMA form   */
                                    /* (see reduce_sum); not with PLAIN or      */
                                    /* TWO_PASS                                 */
-#define ARMX_FLAG_MMA_LEAVES 0x20u /* reduce_sum_fixed_order: the fixed order  */
-                                   /* whose leaves are MFMAs (see there)       */
+#define ARMX_FLAG_MMA_LEAVES 0x20u /* the two fixed-order entry points: the    */
+                                   /* order whose leaves are MFMAs (see        */
+                                   /* reduce_sum_fixed_order)                  */
 
 typedef struct armx_config {
   int block_threads; /* 0 = default; else 64..1024, a multiple of 64.         */
@@ -228,6 +229,12 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  * reduce_sum_fixed_order of that row alone.  It therefore depends on the
  * row's values only: not on rows, on the row's position, on the block size,
  * chain length or grid (batch invariance).  cols == 0 gives +0.0.
+ *
+ * With ARMX_FLAG_MMA_LEAVES every row is summed in the order with MFMA leaves
+ * of reduce_sum_fixed_order instead: exactly reduce_sum_fixed_order of that
+ * row alone with the flag, and batch invariant in the same way.  Rows of at
+ * most 512 values, several to a wavefront load, take one MFMA per lane block
+ * with the other rows' lanes zeroed, so values never meet another row's.
  *
  * x, rows, cols, ld, out as for reduce_rows (ld a multiple of 8 when
  * rows > 1).  ws unused (may be NULL).  block_threads must be a power of

@@ -26,7 +26,8 @@ What it computes:
 * ``fixed_tree_sum`` / ``fixed_tree_row_sums`` -- the prescribed fixed order:
   a balanced binary tree over the inputs (padded to a power of two with -0.0),
   every node one binary32 round-to-nearest-even addition.
-* ``fixed_tree_sum_mma_leaves`` -- the prescribed order with MFMA leaves:
+* ``fixed_tree_sum_mma_leaves`` / ``fixed_tree_row_sums_mma_leaves`` -- the
+  prescribed order with MFMA leaves (per row for the second):
   chunks of 512 values, each one MFMA against ones from zero as reconstructed
   in ``mfma_model`` (16 column sums, then their balanced tree), and the
   balanced tree over the chunks.
@@ -43,11 +44,13 @@ pages, pinned to the model's own definition and to closed forms.
 from .binary16 import decode_table, decode_bits, BINARY16_QUANTUM_EXP
 from .rounding import round_scaled_int, to_binary32, to_binary64
 from .exact import ExactSum, exact_sum, exact_row_sums
-from .tree import fixed_tree_sum, fixed_tree_row_sums, fixed_tree_sum_mma_leaves
+from .tree import (fixed_tree_sum, fixed_tree_row_sums, fixed_tree_sum_mma_leaves,
+                   fixed_tree_row_sums_mma_leaves)
 
 __all__ = [
     "decode_table", "decode_bits", "BINARY16_QUANTUM_EXP",
     "round_scaled_int", "to_binary32", "to_binary64",
     "ExactSum", "exact_sum", "exact_row_sums",
     "fixed_tree_sum", "fixed_tree_row_sums", "fixed_tree_sum_mma_leaves",
+    "fixed_tree_row_sums_mma_leaves",
 ]

@@ -132,3 +132,21 @@ def fixed_tree_sum_mma_leaves(x: np.ndarray) -> np.float32:
         return np.float32(0.0)
     leaves = mma_leaf_values(x)
     return _tree_levels(_pad_pow2(leaves, leaves.size))
+
+
+def fixed_tree_row_sums_mma_leaves(x: np.ndarray) -> np.ndarray:
+    """The MFMA-leaf order applied to every row of a 2-D binary16 array
+    (each row on its own: its own chunks, its own tree); rows of no values
+    give +0.0."""
+    if x.ndim != 2 or x.dtype != np.float16:
+        raise TypeError("fixed_tree_row_sums_mma_leaves expects a 2-D binary16 array")
+    rows, cols = x.shape
+    if cols == 0 or rows == 0:
+        return np.zeros(rows, dtype=np.float32)
+    chunks = -(-cols // 512)
+    xp = np.zeros((rows, chunks * 512), np.float16)
+    xp[:, :cols] = x
+    # (row, chunk, slot group q, column j, value e) -> (row, chunk, column j, K)
+    cols_k = xp.reshape(rows, chunks, 4, 16, 8).transpose(0, 1, 3, 2, 4).reshape(rows, chunks, 16, 32)
+    leaves = _tree_levels(mma_column_sums(cols_k))            # (rows, chunks)
+    return np.ascontiguousarray(_tree_levels(_pad_pow2(leaves, chunks)))

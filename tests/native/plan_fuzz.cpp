@@ -99,7 +99,7 @@ int main(int argc, char** argv) {
     const uint64_t W = uint64_t(p.waves), R = uint64_t(p.r);
     EXPECT(W >= 1 && W <= 16 && R >= 1 && R <= 8, "W %llu R %llu", (unsigned long long)W,
            (unsigned long long)R);
-    EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || op == ARMX_OP_FIXED,
+    EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || op == ARMX_OP_FIXED || op == ARMX_OP_ROWS_FIXED,
            "MMA leaves accepted for op %d", op);
     const bool levels = (p.flags & ARMX_FLAG_MMA_LEVELS) != 0;
     EXPECT(!levels || op == ARMX_OP_SUM, "levels flag accepted for op %d", op);

@@ -128,16 +128,21 @@ def test_mma_levels_config_rules():
 
 
 def test_mma_leaves_config_rules():
-    # the MFMA-leaf order belongs to reduce_sum_fixed_order only
+    # the MFMA-leaf order belongs to the two fixed-order entry points only
     ws = 1 << 24
     assert armx.lib.reduce_sum(FAKE, 10, FAKE, ws, 1 << 20, cfg(mma_leaves=True), None) == -3
     assert armx.lib.reduce_sum_exact(FAKE, 10, FAKE, None, ws, 1 << 20, cfg(mma_leaves=True),
                                      None) == -3
     assert armx.lib.reduce_rows(FAKE, 4, 96, 96, FAKE, None, 0, cfg(mma_leaves=True), None) == -3
-    assert armx.lib.reduce_rows_fixed_order(FAKE, 4, 96, 96, FAKE, None, 0, cfg(mma_leaves=True),
-                                            None) == -3
     assert armx.workspace_bytes(armx.OP_FIXED, 1 << 20, mma_leaves=True) == \
         armx.workspace_bytes(armx.OP_FIXED, 1 << 20)
+    for cols in (96, 512, 520, 1 << 20):
+        assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 4, cols, mma_leaves=True) == 0
+    # the row entry point keeps its other rules with the flag
+    assert armx.lib.reduce_rows_fixed_order(FAKE, 4, 96, 96, FAKE, None, 0,
+                                            cfg(mma_leaves=True, plain=True), None) == -3
+    assert armx.lib.reduce_rows_fixed_order(FAKE, 4, 96, 96, FAKE, None, 0,
+                                            cfg(mma_leaves=True, block_threads=192), None) == -3
 
 
 def test_mma_levels_workspace_sizes():

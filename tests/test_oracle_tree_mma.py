@@ -8,8 +8,8 @@ import pytest
 
 from oracle import exact_sum
 from oracle.mfma_model import chain_column, columns_from_zero
-from oracle.tree import (fixed_tree_sum_mma_leaves, mma_column_sums, mma_leaf_columns,
-                         mma_leaf_values)
+from oracle.tree import (fixed_tree_row_sums_mma_leaves, fixed_tree_sum_mma_leaves,
+                         mma_column_sums, mma_leaf_columns, mma_leaf_values)
 
 import synth_inputs as si
 
@@ -121,3 +121,11 @@ def test_non_finite_values():
 def test_empty_and_leaf_count():
     assert fixed_tree_sum_mma_leaves(np.zeros(0, np.float16)).view(np.uint32) == 0
     assert mma_leaf_values(np.ones(1025, np.float16)).shape == (3,)
+
+
+@pytest.mark.parametrize("cols", [0, 1, 100, 512, 513, 1500, 4096])
+def test_row_sums_are_the_order_applied_to_each_row(cols):
+    x = si.generate_rows("logu_signed", 7, cols, seed=cols)
+    got = fixed_tree_row_sums_mma_leaves(x)
+    want = np.array([fixed_tree_sum_mma_leaves(x[r]) for r in range(7)], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
