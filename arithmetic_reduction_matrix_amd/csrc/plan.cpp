@@ -308,6 +308,8 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     p.xcd_remap = rows_remap(rows, ld);
     if (cols <= kChunk) {
       if (auto_block) p.waves = kShortBlock / 64;
+      if ((c.flags & ARMX_FLAG_MMA_LEAVES) && p.waves > kShortMmaMaxBlock / 64)
+        p.waves = kShortMmaMaxBlock / 64;
       plan_short_rows(p, cu_count, uint64_t(p.waves), c.grid_blocks);
       *plan = p;
       return ARMX_OK;

@@ -101,6 +101,11 @@ constexpr uint64_t kPaceShortChains = 8;
 constexpr int kShortGroups = 8;
 constexpr int kShortWavesPerCu = 4;
 constexpr int kShortBlock = 256;   // automatic block size for such rows
+// Largest block of the MFMA-leaf kernel for such rows: its two reduction
+// paths need more than the 128 registers a 1024-thread block leaves a lane
+// (a larger requested block is lowered to this; a row's result never depends
+// on the block).
+constexpr int kShortMmaMaxBlock = 256;
 
 // MMA levels (ARMX_FLAG_MMA_LEVELS): the number of fp32 values level `level`
 // produces from `count` inputs -- one per chain of R x 512 binary16 values at

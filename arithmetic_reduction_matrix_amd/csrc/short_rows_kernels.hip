@@ -92,8 +92,44 @@ __device__ __forceinline__ float short_row_node(u32x4 t, int lane) {
   }
 }
 
+// The same nodes from one MFMA per load: the A operand, all ones in
+// short_row_node_mma, becomes a selector with A[i][k] = 1 when K position k
+// belongs to the lane block whose lanes receive output row i (lane l holds
+// output rows 4 (l / 16) .. + 3 of column l % 16), else 0.  Every output row
+// then sums only its own block's K groups, the others contributing zero
+// products, so every lane again ends with its own column sum.  A lane
+// supplies A[l % 16][8 (l / 16) .. + 7]: one value for all eight.  Only for
+// finite inputs: 0 x Inf is NaN, which would reach the other blocks' rows in
+// that column (the caller checks).
+template <int S>
+__device__ __forceinline__ half8 block_selector(int lane) {
+  constexpr int B = S < 4 ? 4 : S;
+  const bool on = ((lane >> 4) >> (B - 4)) == (((lane & 15) >> 2) >> (B - 4));
+  const _Float16 v = on ? _Float16(1.0f) : _Float16(0.0f);
+  return half8{v, v, v, v, v, v, v, v};
+}
+
+template <int S>
+__device__ __forceinline__ float short_row_node_sel(u32x4 t, half8 sel) {
+  const floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+      sel, __builtin_bit_cast(half8, t), floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+  return lane_tree(c[0], S < 4 ? S : 4);
+}
+
+// Whether any of this lane's 8 values is an Inf or a NaN (exponent field all
+// ones): the largest masked exponent field of each half-word column.
+__device__ __forceinline__ bool has_non_finite(u32x4 t) {
+  using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+  constexpr uint32_t kExp = 0x7C007C00u;
+  u16x2 m = __builtin_bit_cast(u16x2, t[0] & kExp);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, t[1] & kExp));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, t[2] & kExp));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, t[3] & kExp));
+  return (m[0] == 0x7C00u) | (m[1] == 0x7C00u);
+}
+
 template <int S, bool NT, bool MMA>
-__global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_kernel(const uint16_t* __restrict__ x,
                                                           uint64_t rows, uint64_t cols,
                                                           uint64_t ld, float* __restrict__ out,
                                                           int remap) {
@@ -138,14 +174,36 @@ __global__ __launch_bounds__(1024) void short_rows_kernel(const uint16_t* __rest
     for (int u = 0; u < G; ++u)
       v[u] = load16<NT>(reinterpret_cast<const u32x4*>(x + row_of(c, u) * ld) + read_slot);
   };
+  const half8 sel = block_selector<S>(lane);
   auto reduce_step = [&](uint64_t c, const u32x4 (&v)[G]) {
+    u32x4 t[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      u32x4 t;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) t[w] = (v[u][w] & keep[w]) | (kNegZero2 & ~keep[w]);
-      out[row_of(c, u)] = short_row_node<S, MMA>(t, lane);   // the same in every lane of the row
+      for (int w = 0; w < 4; ++w) t[u][w] = (v[u][w] & keep[w]) | (kNegZero2 & ~keep[w]);
     }
+    // with MFMA leaves: one selector MFMA per load unless the step holds an
+    // Inf or a NaN (then a masked MFMA per lane block); one row per load
+    // (P = 64) needs neither
+    bool one_mfma = MMA && S == 6;
+    if constexpr (MMA && S < 6) {
+      bool nf = false;
+#pragma unroll
+      for (int u = 0; u < G; ++u) nf = nf | has_non_finite(t[u]);
+      one_mfma = __builtin_amdgcn_ballot_w64(nf) == 0;
+    }
+    // no memory access inside the branch: stores there make the compiler wait
+    // for every load in flight where the two paths join
+    float node[G];
+    if (one_mfma) {
+#pragma unroll
+      for (int u = 0; u < G; ++u) node[u] = short_row_node_sel<S>(t[u], sel);
+    } else {
+#pragma unroll
+      for (int u = 0; u < G; ++u) node[u] = short_row_node<S, MMA>(t[u], lane);
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u) out[row_of(c, u)] = node[u];   // the same in every lane of the row
   };
   auto step = [&](uint64_t j) { return g + (j < K ? j : K - 1) * T; };
 
@@ -191,6 +249,8 @@ const void* short_rows_kernel_for(int s, bool nt, bool mma) {
 hipError_t launch_short_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0 || plan.n > kChunk) return hipErrorInvalidValue;
+  if ((plan.flags & ARMX_FLAG_MMA_LEAVES) && plan.waves * 64 > kShortMmaMaxBlock)
+    return hipErrorInvalidValue;
   const void* fn = short_rows_kernel_for(plan.seg_log2, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
                                          (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
   if (!fn) return hipErrorInvalidValue;

@@ -179,6 +179,8 @@ int main(int argc, char** argv) {
         const uint64_t steps = cdiv(p.rows, (64 / P) * armx::kShortGroups);
         EXPECT(uint64_t(p.grid) <= cdiv(steps, W), "short-row grid %d", p.grid);
         EXPECT(p.lds_bytes == 0, "short-row lds");
+        EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || W * 64 <= armx::kShortMmaMaxBlock,
+               "MFMA-leaf short-row block %llu", (unsigned long long)(W * 64));
       }
     }
     if (op == ARMX_OP_ROWS_FIXED) {

@@ -2,7 +2,8 @@
 MFMA-leaf order applied to every row (oracle.tree
 fixed_tree_row_sums_mma_leaves, built on the reconstructed MFMA accumulation
 of oracle.mfma_model), bit for bit: rows of at most 512 values packed several
-to a load (one masked MFMA per lane block), long rows streamed by one
+to a load (one MFMA per load with a K-group selector, or one masked MFMA per
+lane block where a load holds an Inf or a NaN), long rows streamed by one
 wavefront or summed by a block, ragged rows and pitches, non-finite values,
 and batch invariance -- the balanced-tree reproducibility of "Taming Bitwise
 Behavior in GPU Kernels with Tensor Core" (arXiv 2609.11356, Abstract) with
@@ -115,6 +116,25 @@ def test_non_finite_values_stay_in_their_row(cols):
     fin = np.isfinite(want)
     assert fin.sum() == 60
     assert np.array_equal(bits(got[fin]), bits(want[fin]))
+
+
+@pytest.mark.parametrize("cols", [8, 40, 64, 100, 200, 264])
+def test_scattered_non_finite_rows(cols):
+    # most loads take one MFMA with a K-group selector; the few that hold an
+    # Inf or a NaN take one masked MFMA per lane block instead, in the same
+    # launch -- both must give the oracle's bits
+    rows = 20011
+    x = si.generate_rows("logu_signed", rows, cols, seed=cols + 100)
+    rng = np.random.default_rng(cols)
+    bad = rng.choice(rows, 12, replace=False)
+    for k, r in enumerate(bad):
+        x[r, rng.integers(0, cols)] = (np.inf, -np.inf, np.nan)[k % 3]
+    got = mma_rows(strided(x, pitch(cols)))
+    want = fixed_tree_row_sums_mma_leaves(x)
+    fin = np.isfinite(want)
+    assert fin.sum() == rows - 12
+    assert np.array_equal(bits(got[fin]), bits(want[fin]))
+    assert np.array_equal(got[~fin], want[~fin], equal_nan=True)
 
 
 @pytest.mark.parametrize("cols", [24, 130, 512, 3000])
