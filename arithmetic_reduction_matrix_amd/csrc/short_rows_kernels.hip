@@ -175,35 +175,44 @@ __global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_ker
       v[u] = load16<NT>(reinterpret_cast<const u32x4*>(x + row_of(c, u) * ld) + read_slot);
   };
   const half8 sel = block_selector<S>(lane);
+  // values that are not the row's become -0.0
+  auto row_values = [&](const u32x4& v) {
+    u32x4 t;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t[w] = (v[w] & keep[w]) | (kNegZero2 & ~keep[w]);
+    return t;
+  };
   auto reduce_step = [&](uint64_t c, const u32x4 (&v)[G]) {
-    u32x4 t[G];
+    if constexpr (!MMA) {
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) t[u][w] = (v[u][w] & keep[w]) | (kNegZero2 & ~keep[w]);
-    }
-    // with MFMA leaves: one selector MFMA per load unless the step holds an
-    // Inf or a NaN (then a masked MFMA per lane block); one row per load
-    // (P = 64) needs neither
-    bool one_mfma = MMA && S == 6;
-    if constexpr (MMA && S < 6) {
-      bool nf = false;
-#pragma unroll
-      for (int u = 0; u < G; ++u) nf = nf | has_non_finite(t[u]);
-      one_mfma = __builtin_amdgcn_ballot_w64(nf) == 0;
-    }
-    // no memory access inside the branch: stores there make the compiler wait
-    // for every load in flight where the two paths join
-    float node[G];
-    if (one_mfma) {
-#pragma unroll
-      for (int u = 0; u < G; ++u) node[u] = short_row_node_sel<S>(t[u], sel);
+      for (int u = 0; u < G; ++u)   // the same value in every lane of the row
+        out[row_of(c, u)] = lane_tree(leaf8(row_values(v[u])), S);
     } else {
+      u32x4 t[G];
 #pragma unroll
-      for (int u = 0; u < G; ++u) node[u] = short_row_node<S, MMA>(t[u], lane);
+      for (int u = 0; u < G; ++u) t[u] = row_values(v[u]);
+      // one selector MFMA per load unless the step holds an Inf or a NaN (then
+      // a masked MFMA per lane block); one row per load (P = 64) needs neither
+      bool one_mfma = true;
+      if constexpr (S < 6) {
+        bool nf = false;
+#pragma unroll
+        for (int u = 0; u < G; ++u) nf = nf | has_non_finite(t[u]);
+        one_mfma = __builtin_amdgcn_ballot_w64(nf) == 0;
+      }
+      // no memory access inside the branch: stores there make the compiler
+      // wait for every load in flight where the two paths join
+      float node[G];
+      if (one_mfma) {
+#pragma unroll
+        for (int u = 0; u < G; ++u) node[u] = short_row_node_sel<S>(t[u], sel);
+      } else {
+#pragma unroll
+        for (int u = 0; u < G; ++u) node[u] = short_row_node_mma<S>(t[u], lane);
+      }
+#pragma unroll
+      for (int u = 0; u < G; ++u) out[row_of(c, u)] = node[u];
     }
-#pragma unroll
-    for (int u = 0; u < G; ++u) out[row_of(c, u)] = node[u];   // the same in every lane of the row
   };
   auto step = [&](uint64_t j) { return g + (j < K ? j : K - 1) * T; };
 

@@ -84,6 +84,47 @@ def event_timed(torch, fn, iters: int, warmup: int = 5):
     return sum(times) / len(times), times[len(times) // 2]
 
 
+def graph_timed(torch, call, calls: int, reps: int = 5):
+    """Average ms per call of call(i) with `calls` calls captured back to back
+    in one HIP graph and replayed: no host work between the calls, so short
+    kernels are timed with the queue kept full (events around each eager call
+    would time the host's call overhead instead).  Best of `reps` replays."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            call(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    per_call = []
+    for _ in range(reps):
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        g.replay()
+        e_ev.record()
+        torch.cuda.synchronize()
+        per_call.append(s_ev.elapsed_time(e_ev) / calls)
+    del g
+    return min(per_call)
+
+
+def stamped_timed(torch, call, iters: int = 50):
+    """Average ms of one kernel: call(i, start, stop) passes HIP events that the
+    library's dispatch packet stamps around its main kernel."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (s_ev, e_ev) in enumerate(evs):
+        call(i, s_ev, e_ev)
+    torch.cuda.synchronize()
+    return sum(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs) / iters
+
+
 def read_ceiling(torch, bufs, n: int, cus: int, iters: int = 20):
     """Best HBM read rate of the plain load stream of libarmx_probe.so over a
     sweep of launch shapes (dispatch-stamped events, inputs rotated), in GB/s,
@@ -304,10 +345,31 @@ def main() -> int:
         # the small and the large single sums: 2^20 (2 MiB, cache-resident,
         # latency-bound) and 2^30 (2 GiB; timing only, so its values are drawn
         # on the device rather than by the seeded generator)
+        # At 2^20 a call's host overhead (about 10 us) exceeds the kernel, so
+        # the small sums are timed in a captured graph (the rate with the queue
+        # full) and by their own dispatch stamps; the graph's result is checked
+        # against the eager call's bits.
         xs = [torch.from_numpy(si.workload("sum_2p20_u01")).to(dev)]
         xs.append(xs[0].clone())
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum(xs[i & 1]), 500)
-        var["sum_2p20"] = {"ms": ms, "median_ms": med, "gbs": 2 * (1 << 20) / ms / 1e6}
+        small = {
+            "sum_2p20": (armx.reduce_sum, armx.OP_SUM, {}),
+            "fixed_order_2p20": (armx.reduce_sum_fixed_order, armx.OP_FIXED, {}),
+            "exact_2p20": (armx.reduce_sum_exact, armx.OP_EXACT, {}),
+        }
+        for key, (fn, op, kw) in small.items():
+            sws = torch.zeros(max(1, armx.workspace_bytes(op, 1 << 20)), dtype=torch.uint8,
+                              device=dev)
+            sout = torch.empty((), dtype=torch.float32, device=dev)
+            eager = fn(xs[1], workspace=sws, **kw).cpu().numpy()
+            g_ms = graph_timed(torch, lambda i: fn(xs[i & 1], out=sout, workspace=sws, **kw), 200)
+            assert sout.cpu().numpy().view(np.uint32) == eager.view(np.uint32), key
+            k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: fn(
+                xs[i & 1], out=sout, workspace=sws, start_event=s_ev, stop_event=e_ev, **kw))
+            e_ms, _ = event_timed(torch, lambda i: fn(xs[i & 1], out=sout, workspace=sws, **kw),
+                                  200)
+            var[key] = {"ms": g_ms, "gbs": 2 * (1 << 20) / g_ms / 1e6,
+                        "timing": "graph of 200 back-to-back calls",
+                        "kernel_ms": k_ms, "eager_call_ms": e_ms}
         del xs
         xl = torch.empty(1 << 30, dtype=torch.float16, device=dev).uniform_(-1, 1)
         ms, med = event_timed(torch, lambda i: armx.reduce_sum(xl), 50)
