@@ -11,9 +11,10 @@ between two synchronisations); `roofline.achieved` is the algorithmic bytes of
 one launch (2 bytes per element) divided by the average kernel time, measured
 with HIP events that the kernel's own dispatch stamps (hipExtLaunchKernel) on
 the stream it runs on, on every 8th step of the timed region.  `cpu_baseline` is
-the CPU oracle (exact integer sum) timed on this host.  `variants` times the
-other rows of the hot path (MFMA-free design, exact sum, MMA-levels form,
-fixed balanced-tree order, row sums, fixed-order row sums,
+the CPU oracle (exact integer sum) timed on this host; its results also give
+`check`, the errors of the headline and the 2^30 precision-stress sums.
+`variants` times the other rows of the hot path (MFMA-free design, exact sum,
+MMA-levels form, fixed balanced-tree order, row sums, fixed-order row sums,
 one-chain-per-wavefront grids) on their own workloads.
 
 `--levels-sweep` times the recursive all-MMA form (one launch per level)
@@ -177,10 +178,11 @@ def mma_levels_count(n: int, r: int) -> int:
     return k
 
 
-def cpu_baseline(x_np, budget_s: float = 12.0):
+def cpu_baseline(x_np, budget_s: float = 12.0, stress_np=None):
     """The exact-sum oracle on the host: whole passes over the input until
-    `budget_s` of CPU time is spent (at least one pass).  Returns the record
-    and the oracle's result."""
+    `budget_s` of CPU time is spent (at least one pass), then one pass over
+    the 2^30 precision-stress input if given.  Returns the record and the
+    oracle's results (the second None without the stress input)."""
     import oracle
     t0 = time.perf_counter()
     passes = 0
@@ -190,10 +192,16 @@ def cpu_baseline(x_np, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": passes * x_np.size / el, "unit": "elements/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{passes} full pass(es) of oracle.exact_sum over the n=2^28 input "
-                      f"({el:.1f} s, numpy, one thread)"}, e
+    elements = passes * x_np.size
+    sample = f"{passes} full pass(es) of oracle.exact_sum over the n=2^28 input"
+    e_stress = None
+    if stress_np is not None:
+        e_stress = oracle.exact_sum(stress_np)
+        el = time.perf_counter() - t0
+        elements += stress_np.size
+        sample += " and one over the n=2^30 precision-stress input"
+    return {"value": elements / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample} ({el:.1f} s, numpy, one thread)"}, e, e_stress
 
 
 def main() -> int:
@@ -321,6 +329,7 @@ def main() -> int:
         }
 
     # ---- the other rows of the hot path ---------------------------------------
+    stress_np = None   # the 2^30 precision-stress input, drawn with the variants
     if not args.no_variants:
         var = {}
         ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], plain=True), 200)
@@ -377,6 +386,18 @@ def main() -> int:
         ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(xl), 50)
         var["exact_2p30"] = {"ms": ms, "gbs": 2 * (1 << 30) / ms / 1e6}
         del xl
+
+        # the precision-stress input (2^30 values, random signs, magnitudes
+        # log-uniform over 2^-14 .. 2^8): results here, their errors against
+        # the exact sum in `check` (computed in the CPU-baseline leg)
+        stress_np = si.workload("sum_2p30_logu")
+        xs30 = torch.from_numpy(stress_np).to(dev)
+        var["precision_2p30_logu"] = {
+            "mfma": float(armx.reduce_sum(xs30).item()),
+            "plain": float(armx.reduce_sum(xs30, plain=True).item()),
+            "exact_result_bits": int(armx.reduce_sum_exact(xs30).cpu().numpy().view(np.uint32)),
+        }
+        del xs30
 
         xf_np = si.workload("fixed_2p26_u11")
         fbufs = [torch.from_numpy(xf_np).to(dev)]
@@ -501,13 +522,22 @@ def main() -> int:
         record["levels_sweep"] = lv
 
     if not args.no_cpu_baseline:
-        record["cpu_baseline"], e = cpu_baseline(x_np)
+        record["cpu_baseline"], e, e30 = cpu_baseline(x_np, stress_np=stress_np)
         record["check"] = {"exact_sum": e.f64, "abs_err": abs(result - e.f64),
                            "rel_err": abs(result - e.f64) / abs(e.f64)}
         if "variants" in record:
             want = int(np.float32(e.f32).view(np.uint32))
             record["check"]["exact_variant_matches_oracle"] = (
                 record["variants"]["exact_2p28"]["result_bits"] == want)
+        if e30 is not None:
+            p30 = record["variants"]["precision_2p30_logu"]
+            record["check"]["precision_2p30_logu"] = {
+                "exact_sum": e30.f64, "abs_sum": e30.abs_sum,
+                "rel_err_mfma": abs(p30["mfma"] - e30.f64) / abs(e30.f64),
+                "rel_err_plain": abs(p30["plain"] - e30.f64) / abs(e30.f64),
+                "exact_variant_matches_oracle":
+                    p30["exact_result_bits"] == int(np.float32(e30.f32).view(np.uint32)),
+            }
 
     print(json.dumps(record), flush=True)
     return 0
