@@ -257,7 +257,8 @@ def fixed_to_int(fixed) -> int:
     return (hi << 64) + (lo & ((1 << 64) - 1))
 
 
-def _rows_call(fn, x: torch.Tensor, out, cfg: Config, name: str) -> torch.Tensor:
+def _rows_call(fn, op: int, x: torch.Tensor, out, workspace, cfg: Config,
+               name: str) -> torch.Tensor:
     _check_input(x, 2, name)
     rows, cols = x.shape
     if cols > 1 and x.stride(1) != 1:
@@ -270,22 +271,38 @@ def _rows_call(fn, x: torch.Tensor, out, cfg: Config, name: str) -> torch.Tensor
             out = torch.empty(rows, dtype=torch.float32, device=dev)
         elif out.dtype != torch.float32 or out.device != dev or out.numel() < rows:
             raise ValueError(f"{name}: out must be a float32 tensor of {rows} on {dev}")
+        if workspace is None:
+            # few long rows are split over wavefronts of several blocks, which
+            # takes a workspace (none for other shapes)
+            need = lib.armx_workspace_bytes(op, rows, cols, ctypes.byref(cfg))
+            if need == ctypes.c_size_t(-1).value:
+                need = 0   # the call itself reports the configuration error
+            ws = _workspace(dev, stream, need)
+        else:
+            ws = workspace
+        ws_ptr = ws.data_ptr() if ws is not None else None
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
         st = fn(x.data_ptr() if x.numel() else None, rows, cols, ld,
-                out.data_ptr() if rows else None, None, 0, ctypes.byref(cfg), stream)
+                out.data_ptr() if rows else None, ws_ptr, ws_bytes, ctypes.byref(cfg), stream)
     _check(st, name)
     return out
 
 
-def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None, **cfg) -> torch.Tensor:
+def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
     """float32 sum of every row of a 2-D float16 GPU tensor whose rows are
-    contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8."""
-    return _rows_call(lib.reduce_rows, x, out, _config(**cfg), "reduce_rows")
+    contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8.
+    A workspace is used only when there are too few rows to fill the device
+    (then each row is split over several wavefronts); by default one is
+    taken from a per-stream cache."""
+    return _rows_call(lib.reduce_rows, OP_ROWS, x, out, workspace, _config(**cfg),
+                      "reduce_rows")
 
 
 def reduce_rows_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,
-                            **cfg) -> torch.Tensor:
+                            workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
     """Balanced-tree-order float32 sum of every row (as reduce_rows): row r's
     bits depend on row r's values only (batch invariant).  ``mma_leaves=True``
     gives each row the order with MFMA leaves of reduce_sum_fixed_order."""
-    return _rows_call(lib.reduce_rows_fixed_order, x, out, _config(**cfg),
-                      "reduce_rows_fixed_order")
+    return _rows_call(lib.reduce_rows_fixed_order, OP_ROWS_FIXED, x, out, workspace,
+                      _config(**cfg), "reduce_rows_fixed_order")

@@ -74,6 +74,24 @@ int prepare_flat(int op, const void* x, size_t n, float* out, void* ws, size_t w
   return check_ws(*plan, ws, ws_bytes);
 }
 
+// Common checks and planning of the two row entry points.  The plan may split
+// few rows over wavefronts of several blocks (mode 3), which needs the
+// workspace; without one (ws NULL) it is made again without that mode.
+int prepare_rows(int op, const void* x, size_t rows, size_t cols, size_t ld, float* out,
+                 void* ws, size_t ws_bytes, const armx_config* cfg, armx::Plan* plan) {
+  if (rows > 0 && !out) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
+  if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  // configuration errors are reported before touching the device
+  armx::Plan probe;
+  int st = armx::make_plan(op, rows, cols, ld, cfg, 256, &probe);
+  if (st != ARMX_OK) return st;
+  const int cus = rows > 0 && cols > 0 ? current_cu_count() : 256;
+  st = armx::make_plan(op, rows, cols, ld, cfg, cus, plan, ws != nullptr);
+  if (st != ARMX_OK) return st;
+  return check_ws(*plan, ws, ws_bytes);
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,39 +129,21 @@ int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, vo
 
 int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, void* ws,
                 size_t ws_bytes, const armx_config* cfg, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  if (rows > 0 && !out) return ARMX_ERR_NULL;
-  if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
-  if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
-  // configuration errors are reported before touching the device
-  armx::Plan probe;
-  int st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg, 256, &probe);
-  if (st != ARMX_OK) return st;
   armx::Plan plan;
-  st = armx::make_plan(armx::kOpRows, rows, cols, ld, cfg,
-                       rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
+  const int st = prepare_rows(armx::kOpRows, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
   log_plan("reduce_rows", plan);
-  return hip_status(armx::launch_rows(plan, x, out, static_cast<hipStream_t>(stream)));
+  return hip_status(armx::launch_rows(plan, x, out, ws, static_cast<hipStream_t>(stream)));
 }
 
 int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
                             void* ws, size_t ws_bytes, const armx_config* cfg, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
-  if (rows > 0 && !out) return ARMX_ERR_NULL;
-  if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
-  if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
-  armx::Plan probe;
-  int st = armx::make_plan(armx::kOpRowsFixed, rows, cols, ld, cfg, 256, &probe);
-  if (st != ARMX_OK) return st;
   armx::Plan plan;
-  st = armx::make_plan(armx::kOpRowsFixed, rows, cols, ld, cfg,
-                       rows > 0 && cols > 0 ? current_cu_count() : 256, &plan);
+  const int st =
+      prepare_rows(armx::kOpRowsFixed, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plan);
   if (st != ARMX_OK) return st;
   log_plan("reduce_rows_fixed_order", plan);
-  return hip_status(armx::launch_rows_fixed(plan, x, out, static_cast<hipStream_t>(stream)));
+  return hip_status(armx::launch_rows_fixed(plan, x, out, ws, static_cast<hipStream_t>(stream)));
 }
 
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_config* cfg) {
@@ -151,9 +151,12 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_co
   if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED &&
       op != ARMX_OP_ROWS_FIXED && op != ARMX_OP_EXACT)
     return size_t(-1);
-  const int cus = (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED || n_or_rows == 0)
-                      ? 256 : current_cu_count();
-  if (armx::make_plan(op, n_or_rows, cols, cols, cfg, cus, &plan) != ARMX_OK) return size_t(-1);
+  const bool rows_op = op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED;
+  const bool empty = n_or_rows == 0 || (rows_op && cols == 0);
+  const int cus = empty ? 256 : current_cu_count();
+  // the row pitch does not change the workspace; take the smallest valid one
+  const size_t ld = rows_op && n_or_rows > 1 ? (cols + 7) / 8 * 8 : cols;
+  if (armx::make_plan(op, n_or_rows, cols, ld, cfg, cus, &plan) != ARMX_OK) return size_t(-1);
   return plan.ws_bytes;
 }
 
@@ -170,6 +173,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 5; }
+int armx_version(void) { return 6; }
 
 }  // extern "C"

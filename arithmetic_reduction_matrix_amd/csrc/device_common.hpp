@@ -480,6 +480,65 @@ __device__ __forceinline__ float load_published(const float* slot) {
   return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The last block of a split row reduction (rows x S parts published by
+// wavefronts of many blocks, parts[r S + j] for j < S): stages every part in
+// LDS (`stage`, at least rows x S floats) with eight loads in flight per
+// thread, then writes out[r] = the balanced tree over row r's S parts in
+// index order, padded with -0.0 to P, the power of two at or above S.  For
+// P <= 64 a group of P lanes takes a row (64 / P rows per wavefront at a
+// time); above, a wavefront takes a row with k = P / 64 parts per lane (at
+// most 8), added pairwise in registers first.  Called by every thread.
+__device__ inline void combine_split_rows(const float* parts, uint64_t rows, unsigned S,
+                                          float* __restrict__ out, float* stage) {
+  const uint64_t items = rows * S;
+  const uint64_t nt = blockDim.x;
+  for (uint64_t base = threadIdx.x; base < items; base += 8 * nt) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t i = base + uint64_t(j) * nt;
+      v[j] = i < items ? load_published(parts + i) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint64_t i = base + uint64_t(j) * nt;
+      if (i < items) stage[i] = v[j];
+    }
+  }
+  __syncthreads();
+  int lp = 0;
+  while ((1u << lp) < S) ++lp;
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  if (lp <= 6) {
+    const uint64_t P = uint64_t(1) << lp, per_wave = uint64_t(64) >> lp;
+    for (uint64_t r0 = uint64_t(wave_id()) * per_wave; r0 < rows; r0 += W * per_wave) {
+      const uint64_t r = r0 + uint64_t(lane) / P, j = uint64_t(lane) % P;
+      float v = r < rows && j < S ? stage[r * S + j] : -0.0f;
+      v = lane_tree(v, lp);
+      if (j == 0 && r < rows) out[r] = v;
+    }
+  } else {
+    const uint64_t k = uint64_t(1) << (lp - 6);
+    for (uint64_t r = uint64_t(wave_id()); r < rows; r += W) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t i = uint64_t(lane) * k + uint64_t(j);
+        v[j] = uint64_t(j) < k && i < S ? stage[r * S + i] : -0.0f;
+      }
+      // registers past k hold -0.0 subtrees, which leave every node unchanged
+#pragma unroll
+      for (int st = 1; st < 8; st *= 2) {
+#pragma unroll
+        for (int j = 0; j < 8; j += 2 * st) v[j] = v[j] + v[j + st];
+      }
+      const float root = lane_tree_full(v[0]);
+      if (lane == 0) out[r] = root;
+    }
+  }
+}
+
 // Two-level completion.  Blocks form groups of `group` consecutive blocks (a
 // power of two, at most kTicketGroups groups); each group has its own counter
 // and the groups a top counter, so no counter sees more than a few dozen

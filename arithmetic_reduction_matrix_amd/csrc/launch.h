@@ -63,11 +63,14 @@ hipError_t launch_exact(const Plan& plan, const void* x, float* out, int64_t* ou
 hipError_t launch_fixed(const Plan& plan, const void* x, float* out, void* ws,
                         hipStream_t stream);
 
-// out[r] = sum of row r, r < plan.rows.
-hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t stream);
+// out[r] = sum of row r, r < plan.rows; ws (the counter and the segment
+// partials) is used by plan mode 3 only.
+hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
+                       hipStream_t stream);
 
-// out[r] = balanced-tree sum of row r, r < plan.rows.
-hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStream_t stream);
+// out[r] = balanced-tree sum of row r, r < plan.rows; ws as for launch_rows.
+hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, void* ws,
+                             hipStream_t stream);
 
 // out[r] = balanced-tree sum of row r, r < plan.rows, for rows of at most one
 // chunk (plan mode 2); serves both row entry points.

@@ -22,6 +22,32 @@ int log2_ceil(uint64_t v) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+int log2_floor(uint64_t v) {
+  int k = 0;
+  while (v > 1) {
+    v >>= 1;
+    ++k;
+  }
+  return k;
+}
+
+// Whether `blocks` blocks spread evenly over the compute units.
+bool even_blocks(uint64_t blocks, int cu_count) {
+  return blocks <= uint64_t(cu_count) || blocks % uint64_t(cu_count) == 0;
+}
+
+// Wavefronts per block of a split (mode 3) with an automatic block size: the
+// part count over the compute-unit count, rounded up (1 to kMaxWaves), so
+// that no compute unit gets a second block -- measured on MI355X, a grid a
+// little larger than the compute-unit count finishes when its doubly loaded
+// units do, up to half again as late.
+uint64_t split_block(uint64_t items, int cu_count) {
+  uint64_t w = ceil_div(items, uint64_t(cu_count));
+  if (w < 1) w = 1;
+  if (w > uint64_t(kMaxWaves)) w = uint64_t(kMaxWaves);
+  return w;
+}
+
 // Blocks of W wavefronts an automatic persistent grid uses: about
 // loads_per_cu / R wavefronts per compute unit, at least one block per unit.
 uint64_t persistent_blocks(const OpDefaults& d, int cu_count, uint64_t W, uint64_t R) {
@@ -135,7 +161,7 @@ void size_ticket(Plan& p, size_t record_bytes = sizeof(float)) {
 }  // namespace
 
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
-              const armx_config* cfg, int cu_count, Plan* plan) {
+              const armx_config* cfg, int cu_count, Plan* plan, bool allow_split) {
   armx_config c{};
   if (cfg) c = *cfg;
   const bool auto_r = c.chain_r == 0;
@@ -275,8 +301,10 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
       p.r = int(R);
       p.waves = int(W);
     }
-    // many rows: one wavefront per row over a persistent grid; few rows: a
-    // block per row so that every row still gets W wavefronts
+    // many rows: one wavefront per row over a persistent grid; few rows:
+    // each row split over wavefronts of several blocks (mode 3, with a
+    // workspace) or, without one, a block per row so that every row still
+    // gets W wavefronts
     const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
     const uint64_t waves = blocks * W;
     uint64_t grid;
@@ -287,6 +315,40 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     } else {
       p.mode = 0;
       grid = rows;
+      const uint64_t cpr = ceil_div(cols, R * kChunk);   // chains per row
+      if (allow_split && rows > 0 && 4 * rows * W < 3 * waves && cols / W >= kSplitMinShare) {
+        // the row's chains are dealt round-robin to its S wavefronts
+        uint64_t S = ceil_div(waves, rows);
+        S = S < cpr ? S : cpr;
+        S = S < cols / kSplitMinSegment ? S : cols / kSplitMinSegment;
+        const uint64_t W3 = auto_block ? split_block(rows * S, cu_count) : W;
+        uint64_t cap = kSplitMaxBlocks;
+        if (c.grid_blocks > 0 && uint64_t(c.grid_blocks) < cap) cap = uint64_t(c.grid_blocks);
+        if (ceil_div(rows * S, W3) > cap) S = cap * W3 / rows;
+        if (S >= 2) {
+          p.mode = 3;
+          p.waves = int(W3);
+          p.segs = unsigned(S);
+          p.grid = int(ceil_div(rows * S, W3));
+          p.partials_bytes = round_up(sizeof(float) * size_t(rows * S), 256);
+          p.ws_bytes = kCounterBytes + p.partials_bytes;
+          *plan = p;
+          return ARMX_OK;
+        }
+      }
+      // a block per row (no workspace); with an automatic block size, rows
+      // that give the persistent grid's wavefront count less than three
+      // quarters get about that count's share each (any W: the row's chains
+      // are dealt round-robin; at most one wavefront per chain) -- when the
+      // blocks spread evenly over the compute units (measured on MI355X:
+      // wider blocks on a grid a little larger than the unit count lose)
+      if (auto_block && rows > 0 && even_blocks(rows, cu_count) && 4 * rows * W < 3 * waves) {
+        uint64_t w = ceil_div(waves, rows);
+        if (w > cpr) w = cpr;
+        if (w > uint64_t(kMaxWaves)) w = uint64_t(kMaxWaves);
+        if (w > W) W = w;
+        p.waves = int(W);
+      }
     }
     if (grid > (uint64_t(1) << 20)) grid = uint64_t(1) << 20;   // blocks loop over rows
     if (c.grid_blocks > 0 && grid > uint64_t(c.grid_blocks)) grid = uint64_t(c.grid_blocks);
@@ -322,10 +384,75 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
       p.r = int(R);
       p.waves = int(W);
     }
-    const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
+    uint64_t blocks = persistent_blocks(d, cu_count, W, R);
     const uint64_t group_elems = R * kChunk;
+    bool flat = is_pow2(R) && ceil_div(cols, group_elems) <= 64 && (rows >= blocks * W || W == 1);
+    // Rows that give the persistent grid's wavefront count less than three
+    // quarters: split each row into S aligned power-of-two chunk ranges
+    // (subtrees), one wavefront each in blocks of W3; the last block's tree
+    // over a row's S segment roots is the row's tree.  The range size is the
+    // largest power of two that still gives at least the grid's wavefront
+    // count of ranges in all, so no wavefront holds more than its share (a
+    // row's last range may be short).  The ranges are long, so an automatic
+    // R is the flat fixed-order sum's 8.
+    const uint64_t per_row = flat ? 1 : W;
+    if (allow_split && 4 * rows * per_row < 3 * blocks * W && cols / per_row >= kSplitMinShare) {
+      const uint64_t R3 = auto_r ? uint64_t(kFixedDefaults.r) : R;
+      const uint64_t waves3 = persistent_blocks(d, cu_count, 1, R3);
+      const uint64_t chunks = ceil_div(cols, kChunk);
+      const uint64_t per_node = is_pow2(R3) ? R3 : 1;
+      auto segs_for = [&](int l) { return ceil_div(chunks, uint64_t(1) << l); };
+      auto slots_for = [&](int l) {
+        return (ceil_div(uint64_t(1) << l, per_node) + 63) / 64 * 64;
+      };
+      const int min_lc = log2_ceil(kSplitMinSegment / kChunk);
+      int lc = rows * chunks >= waves3 ? log2_floor(rows * chunks / waves3) : 0;
+      if (lc < min_lc) lc = min_lc;
+      while (segs_for(lc) > kSplitMaxSegs || rows * segs_for(lc) > kSplitMaxItems) ++lc;
+      const uint64_t W3 = auto_block ? split_block(rows * segs_for(lc), cu_count) : W;
+      uint64_t cap = kSplitMaxBlocks;
+      if (c.grid_blocks > 0 && uint64_t(c.grid_blocks) < cap) cap = uint64_t(c.grid_blocks);
+      while (ceil_div(rows * segs_for(lc), W3) > cap && segs_for(lc) > 1) ++lc;
+      // node logs, beside the last block's stage of parts: fewer chunks per
+      // segment (more segments) while they do not fit
+      const size_t log_bytes = kFixedLdsBytes - kSplitMaxItems * sizeof(float);
+      while (W3 * slots_for(lc) * sizeof(float) > log_bytes && lc > min_lc &&
+             segs_for(lc - 1) <= kSplitMaxSegs && ceil_div(rows * segs_for(lc - 1), W3) <= cap)
+        --lc;
+      const uint64_t S = segs_for(lc);
+      if (S >= 2 && lc <= kFixedMaxLog2Chunks &&
+          W3 * slots_for(lc) * sizeof(float) <= log_bytes) {
+        p.mode = 3;
+        p.r = int(R3);
+        p.waves = int(W3);
+        p.segs = unsigned(S);
+        p.log2_chunks = lc;
+        p.slots_per_wave = unsigned(slots_for(lc));
+        p.lds_bytes = size_t(W3 * slots_for(lc) * sizeof(float));
+        p.grid = int(ceil_div(rows * S, W3));
+        p.partials_bytes = round_up(sizeof(float) * size_t(rows * S), 256);
+        p.ws_bytes = kCounterBytes + p.partials_bytes;
+        *plan = p;
+        return ARMX_OK;
+      }
+    }
+    // otherwise, with an automatic block size, rows that give the persistent
+    // grid's wavefront count less than three quarters get more wavefronts
+    // each (the general mapping, W per row; measured on MI355X, a fixed-order
+    // wavefront at R = 4 keeps fewer bytes in flight than a free-order one)
+    if (auto_block && rows < blocks * W && even_blocks(rows, cu_count)) {
+      const uint64_t target = blocks * W, chunks = ceil_div(cols, kChunk);
+      uint64_t W2 = W;
+      while (4 * rows * W2 < 3 * target && 2 * W2 <= chunks && W2 < uint64_t(kMaxWaves)) W2 *= 2;
+      if (W2 != W) {
+        W = W2;
+        p.waves = int(W);
+        blocks = persistent_blocks(d, cu_count, W, R);
+        flat = false;
+      }
+    }
     uint64_t grid;
-    if (is_pow2(R) && ceil_div(cols, group_elems) <= 64 && (rows >= blocks * W || W == 1)) {
+    if (flat) {
       // flat: a wavefront's rows stream back to back; each row is at most
       // 64 group subtrees, one per lane of a slot register
       p.mode = 1;

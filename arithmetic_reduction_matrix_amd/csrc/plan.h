@@ -70,8 +70,11 @@ struct Plan {
   int log2_chunks = 0;      // fixed order: 2^log2_chunks chunks per wavefront
   int mode = 0;             // rows: 1 = one wavefront per row, 0 = one block per row;
                             // fixed-order rows: 1 = flat (cross-row stream), 0 = general;
-                            // both: 2 = rows of at most one chunk, segmented lanes
+                            // both: 2 = rows of at most one chunk, segmented lanes;
+                            // 3 = each row split over `segs` wavefronts of several
+                            // blocks, combined by the last block (a workspace)
   int seg_log2 = 0;         // mode 2: log2 of the lanes per row (a power of two)
+  unsigned segs = 0;        // mode 3: wavefronts (row segments) per row
   int xcd_remap = 0;        // rows: give each XCD a contiguous range of block ids
   unsigned slots_per_wave = 0;  // fixed order: LDS floats of each wavefront's node log
   size_t lds_bytes = 0;     // dynamic LDS per block
@@ -107,6 +110,26 @@ constexpr int kShortBlock = 256;   // automatic block size for such rows
 // on the block).
 constexpr int kShortMmaMaxBlock = 256;
 
+// Rows too few to give the persistent grid's wavefronts one row each (mode
+// 3): every row is split over several wavefronts in different blocks, each
+// publishing a partial result; one completion counter (the grid is at most
+// kSplitMaxBlocks blocks, within what the flat sums' single-level ticket
+// takes) lets the last block stage all rows x S partials (at most
+// kSplitMaxItems) in LDS and combine every row's.  An automatic block size
+// is the part count over the compute-unit count (not a power of two), so
+// the grid keeps every compute unit busy.  Fixed order splits a row
+// into at most kSplitMaxSegs aligned power-of-two chunk ranges (the tree over
+// a row's segment roots holds 8 per lane).
+// A split pays for its completion ticket (a few microseconds) only when a
+// wavefront's share of a row without it is large: at least kSplitMinShare
+// values (64 KiB); no segment is made smaller than kSplitMinSegment values.
+constexpr uint64_t kSplitMaxBlocks = 512;
+constexpr uint64_t kSplitMaxItems = 8192;
+static_assert(kSplitMaxItems == kSplitMaxBlocks * kMaxWaves, "a split grid's parts fit the stage");
+constexpr uint64_t kSplitMaxSegs = 512;
+constexpr uint64_t kSplitMinShare = 32768;
+constexpr uint64_t kSplitMinSegment = 8192;
+
 // MMA levels (ARMX_FLAG_MMA_LEVELS): the number of fp32 values level `level`
 // produces from `count` inputs -- one per chain of R x 512 binary16 values at
 // level 1, one per chain of R x 256 fp32 values above.
@@ -116,9 +139,10 @@ inline uint64_t level_count(uint64_t count, uint64_t r, int level) {
 }
 
 // Resolves and checks a configuration for `op`.  `cu_count` is the number of
-// compute units of the target device.  Returns ARMX_OK or a negative status;
-// pointers are not examined here.
+// compute units of the target device.  `allow_split` lets the row entry
+// points plan mode 3 (which needs a workspace).  Returns ARMX_OK or a
+// negative status; pointers are not examined here.
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
-              const armx_config* cfg, int cu_count, Plan* plan);
+              const armx_config* cfg, int cu_count, Plan* plan, bool allow_split = true);
 
 }  // namespace armx

@@ -28,6 +28,11 @@
 //    of two) take aligned power-of-two chunk ranges of the row and reduce
 //    them as the flat fixed-order kernel does; the W roots are combined by a
 //    lane tree.
+//  * split (few rows, with a workspace): every row is cut into S aligned
+//    ranges of 2^c chunks, one wavefront each in blocks spread over the
+//    device; each range's subtree root is published, and the last block to
+//    finish takes, for every row, the balanced tree over its S roots (padded
+//    with -0.0), which is the row's tree above those subtrees.
 // MMA selects the order with MFMA leaves (every chunk node one
 // v_mfma_f32_16x16x32_f16 against ones and the tree over its 16 column sums,
 // as for the flat fixed-order sum), per row.  A chunk that lies wholly past
@@ -197,6 +202,44 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
   }
 }
 
+// Few rows: wavefront `item` (block * W + wave) reduces range s = item % S of
+// row item / S (chunks s 2^log2c .. + 2^log2c, cut at the row's end, values
+// past the row -0.0) to its subtree root, publishes it in partials[item],
+// and the last block writes out[r] = the balanced tree over row r's S roots
+// padded with -0.0 (combine_split_rows): the row's tree above its ranges.
+template <int R, bool NT, bool MMA>
+__global__ __launch_bounds__(1024) void rows_fixed_split_kernel(
+    const uint16_t* __restrict__ x, uint64_t rows, uint64_t cols, uint64_t ld,
+    float* __restrict__ out, unsigned segs, int log2c, unsigned slots_per_wave,
+    unsigned* __restrict__ counter, float* __restrict__ partials) {
+  __shared__ int flag;
+  __shared__ float stage[kSplitMaxItems];
+  extern __shared__ float node_lds[];
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t S = segs;
+  const uint64_t item = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
+  if (item < rows * S) {
+    const uint64_t row = item / S, s = item % S;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + row * ld);
+    const uint64_t chunks = (cols + 511) / 512;
+    const uint64_t first = s << log2c;
+    const uint64_t span = uint64_t(1) << log2c;
+    const uint64_t valid = chunks - first < span ? chunks - first : span;
+    float* log_rows = node_lds + unsigned(wave_id()) * slots_per_wave;
+    const float root =
+        valid / R >= kPaceLongChains
+            ? wave_range_root<R, NT, 2, MMA>(xr, cols, first, valid, lane, log_rows)
+            : wave_range_root<R, NT, 0, MMA>(xr, cols, first, valid, lane, log_rows);
+    if (lane == 0) __hip_atomic_store(partials + item, root, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the root is stored
+  }
+  __syncthreads();   // every wavefront's root is stored before the block counts
+  if (!publish_with_ticket([] {}, counter, gridDim.x, &flag)) return;
+  combine_split_rows(partials, rows, segs, out, stage);
+}
+
 template <int R>
 const void* pick_rows_fixed(bool nt, bool mma) {
   if (mma)
@@ -220,12 +263,51 @@ const void* rows_fixed_kernel_for(int r, bool nt, bool mma) {
   }
 }
 
+template <int R>
+const void* pick_split(bool nt, bool mma) {
+  if (mma)
+    return nt ? reinterpret_cast<const void*>(&rows_fixed_split_kernel<R, true, true>)
+              : reinterpret_cast<const void*>(&rows_fixed_split_kernel<R, false, true>);
+  return nt ? reinterpret_cast<const void*>(&rows_fixed_split_kernel<R, true, false>)
+            : reinterpret_cast<const void*>(&rows_fixed_split_kernel<R, false, false>);
+}
+
+const void* rows_fixed_split_kernel_for(int r, bool nt, bool mma) {
+  switch (r) {
+    case 1: return pick_split<1>(nt, mma);
+    case 2: return pick_split<2>(nt, mma);
+    case 3: return pick_split<3>(nt, mma);
+    case 4: return pick_split<4>(nt, mma);
+    case 5: return pick_split<5>(nt, mma);
+    case 6: return pick_split<6>(nt, mma);
+    case 7: return pick_split<7>(nt, mma);
+    case 8: return pick_split<8>(nt, mma);
+    default: return nullptr;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, hipStream_t stream) {
+hipError_t launch_rows_fixed(const Plan& plan, const void* x, float* out, void* ws,
+                             hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
   if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
+  if (plan.mode == 3) {
+    const void* fn = rows_fixed_split_kernel_for(plan.r,
+                                                 (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                                 (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
+    if (!fn || !ws) return hipErrorInvalidValue;
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
+    unsigned segs = plan.segs;
+    int log2c = plan.log2_chunks;
+    unsigned slots_per_wave = plan.slots_per_wave;
+    Workspace w = workspace_layout(plan, ws);
+    void* args[] = {&xh,  &rows,           &cols,       &ld,        &out,
+                    &segs, &log2c, &slots_per_wave, &w.counters, &w.partials};
+    return launch_main(plan, fn, args, stream);
+  }
   const void* fn = rows_fixed_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
                                          (plan.flags & ARMX_FLAG_MMA_LEAVES) != 0);
   if (!fn) return hipErrorInvalidValue;

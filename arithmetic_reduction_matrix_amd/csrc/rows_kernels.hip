@@ -15,6 +15,11 @@
 //    last partial chain is masked in registers (the matrix's last row then
 //    takes exact masked loads instead); no block synchronisation at all.
 //    Used when there are many rows.
+//  * rows_split_kernel (few rows, with a workspace): every row is split over
+//    S wavefronts of several blocks, which take the row's chains
+//    round-robin as the flat sum's wavefronts take the input's, each with
+//    its own paced pipeline; each publishes its partial, and the last block
+//    to finish adds every row's S partials in index order.
 //  * otherwise each block sums a row (looping over rows if needed) and its W
 //    wavefronts take the row's chains round-robin, combined through LDS.
 #include "device_common.hpp"
@@ -153,6 +158,53 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
   }
 }
 
+// Few rows: wavefront `item` (block * W + wave) is segment s = item % S of row
+// item / S and takes that row's chains s, s + S, ...; the row's partial
+// chain (if any) goes to the wavefront whose turn it is, with exact masked
+// loads.  Partials go to partials[item]; one completion counter, and the last
+// block writes out[r] = the balanced tree over row r's S partials in index
+// order (combine_split_rows), so the result depends on the configuration
+// only.
+template <int R, bool NT, bool PLAIN>
+__global__ __launch_bounds__(1024) void rows_split_kernel(const uint16_t* __restrict__ x,
+                                                          uint64_t rows, uint64_t cols,
+                                                          uint64_t ld, float* __restrict__ out,
+                                                          unsigned segs,
+                                                          unsigned* __restrict__ counter,
+                                                          float* __restrict__ partials) {
+  __shared__ int flag;
+  __shared__ float stage[kSplitMaxItems];
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t S = segs;
+  const uint64_t item = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
+  if (item < rows * S) {
+    const uint64_t row = item / S, s = item % S;
+    const uint16_t* xr = x + row * ld;
+    const u32x4* xv = reinterpret_cast<const u32x4*>(xr);
+    const uint64_t chains_full = cols / (uint64_t(R) * 512);
+    const uint64_t iters = s < chains_full ? (chains_full - 1 - s) / S + 1 : 0;
+    float run = 0.0f;
+    // pacing as for the flat sum
+    if (iters >= kPaceLongChains) {
+      stream_chains<R, NT, PLAIN, PLAIN ? 4 : 8>(xv, s, iters, S, lane, run);
+    } else if (!PLAIN && iters >= kPaceShortChains) {
+      stream_chains<R, NT, PLAIN, 2>(xv, s, iters, S, lane, run);
+    } else {
+      stream_chains<R, NT, PLAIN>(xv, s, iters, S, lane, run);
+    }
+    if (chains_full * R * 512 < cols && s + iters * S == chains_full)
+      tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
+    const float total = wave_total<PLAIN>(run);
+    if (lane == 0) __hip_atomic_store(partials + item, total, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial is stored
+  }
+  __syncthreads();   // every wavefront's partial is stored before the block counts
+  if (!publish_with_ticket([] {}, counter, gridDim.x, &flag)) return;
+  combine_split_rows(partials, rows, segs, out, stage);
+}
+
 template <int R, bool NT, bool PLAIN>
 const void* rows_ptr() {
   return reinterpret_cast<const void*>(&rows_kernel<R, NT, PLAIN>);
@@ -178,12 +230,49 @@ const void* rows_kernel_for(int r, bool nt, bool plain) {
   }
 }
 
+template <int R, bool NT, bool PLAIN>
+const void* split_ptr() {
+  return reinterpret_cast<const void*>(&rows_split_kernel<R, NT, PLAIN>);
+}
+
+template <int R>
+const void* pick_split(bool nt, bool plain) {
+  if (nt) return plain ? split_ptr<R, true, true>() : split_ptr<R, true, false>();
+  return plain ? split_ptr<R, false, true>() : split_ptr<R, false, false>();
+}
+
+const void* rows_split_kernel_for(int r, bool nt, bool plain) {
+  switch (r) {
+    case 1: return pick_split<1>(nt, plain);
+    case 2: return pick_split<2>(nt, plain);
+    case 3: return pick_split<3>(nt, plain);
+    case 4: return pick_split<4>(nt, plain);
+    case 5: return pick_split<5>(nt, plain);
+    case 6: return pick_split<6>(nt, plain);
+    case 7: return pick_split<7>(nt, plain);
+    case 8: return pick_split<8>(nt, plain);
+    default: return nullptr;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_rows(const Plan& plan, const void* x, float* out, hipStream_t stream) {
+hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
+                       hipStream_t stream) {
   if (plan.rows == 0) return hipSuccess;
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
   if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
+  if (plan.mode == 3) {
+    const void* fn = rows_split_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                           (plan.flags & ARMX_FLAG_PLAIN) != 0);
+    if (!fn || !ws) return hipErrorInvalidValue;
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
+    unsigned segs = plan.segs;
+    Workspace w = workspace_layout(plan, ws);
+    void* args[] = {&xh, &rows, &cols, &ld, &out, &segs, &w.counters, &w.partials};
+    return launch_main(plan, fn, args, stream);
+  }
   const void* fn = rows_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
                                    (plan.flags & ARMX_FLAG_PLAIN) != 0);
   if (!fn) return hipErrorInvalidValue;

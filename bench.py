@@ -444,6 +444,17 @@ def main() -> int:
                 ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
                 var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
             del views, vout
+        # few long rows, each split over wavefronts of several blocks
+        for nrows in (1, 8):
+            cols = n // nrows
+            views = [b.view(nrows, cols) for b in bufs]
+            vout = torch.empty(nrows, dtype=torch.float32, device=dev)
+            moved = 2 * n + 4 * nrows
+            for tag, fn in (("rows", armx.reduce_rows),
+                            ("rows_fixed_order", armx.reduce_rows_fixed_order)):
+                ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
+                var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
+            del views, vout
         record["variants"] = var
 
     if args.copy_calibration:

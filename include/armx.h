@@ -170,9 +170,16 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
  * cols     elements summed per row (0 writes +0.0 to every row).
  * ld       row pitch in elements, ld >= cols.
  * out      device, rows binary32 values.
- * ws       unused (armx_workspace_bytes returns 0); may be NULL.
+ * ws       device workspace (see conventions), or NULL.  When the rows are
+ *          too few for the device (fewer than the wavefronts of its
+ *          persistent grid) and long, armx_workspace_bytes is non-zero and,
+ *          with a workspace, every row is split over several wavefronts in
+ *          different blocks whose partial sums the last block to finish
+ *          adds in index order; with ws NULL each such row is summed by one
+ *          block instead (slower, and in another order).  Otherwise ws is
+ *          not used.
  * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
- * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  *
  * Rows of at most 512 values are summed by lanes (each row on a
  * power-of-two group of lanes, several rows per wavefront load) in the
@@ -238,12 +245,16 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  * most 512 values, several to a wavefront load, take one MFMA per lane block
  * with the other rows' lanes zeroed, so values never meet another row's.
  *
- * x, rows, cols, ld, out as for reduce_rows (ld a multiple of 8 when
- * rows > 1).  ws unused (may be NULL).  block_threads must be a power of
+ * x, rows, cols, ld, out, ws as for reduce_rows (ld a multiple of 8 when
+ * rows > 1).  With a workspace, few long rows are split into aligned
+ * power-of-two chunk ranges (complete subtrees) over wavefronts of several
+ * blocks, and the last block takes each row's tree over its ranges' roots:
+ * the same bits as any other mapping.  block_threads must be a power of
  * two.  ARMX_FLAG_PLAIN, ARMX_FLAG_ONE_CHAIN and ARMX_FLAG_TWO_PASS are not
- * accepted.  Rows longer than the LDS node logs allow (about 2^26 values at
- * R = 8, 2^25 at the default R = 4, 2^23 at R = 1) return ARMX_ERR_SHAPE.
- * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP}.
+ * accepted.  Without a split (ws NULL, or enough rows), rows longer than the
+ * LDS node logs allow (about 2^26 values at R = 8, 2^25 at the default
+ * R = 4, 2^23 at R = 1) return ARMX_ERR_SHAPE.
+ * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  */
 int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
                             void* ws, size_t ws_bytes, const armx_config* cfg, void* stream);
@@ -299,7 +310,7 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 5. */
+/* armx_version -- ABI version of this header: 6. */
 int armx_version(void);
 
 #ifdef __cplusplus

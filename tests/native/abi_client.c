@@ -38,7 +38,7 @@ static int failures = 0;
 static int cpu_checks(void) {
   char* fake = (char*)(uintptr_t)(1u << 20); /* never dereferenced */
   armx_config bad = {96, 0, 0, 0, NULL, NULL};
-  EXPECT(armx_version() == 5);
+  EXPECT(armx_version() == 6);
   EXPECT(reduce_sum(NULL, 10, (float*)fake, fake, 1 << 20, NULL, NULL) == ARMX_ERR_NULL);
   EXPECT(reduce_sum(fake + 2, 10, (float*)fake, fake, 1 << 20, NULL, NULL) == ARMX_ERR_ALIGN);
   EXPECT(reduce_sum(fake, 10, (float*)fake, fake, 1 << 20, &bad, NULL) == ARMX_ERR_CONFIG);

@@ -163,7 +163,28 @@ int main(int argc, char** argv) {
     }
     if (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED) {
       EXPECT(p.ld >= p.n, "ld");
-      EXPECT(p.ws_bytes == 0, "rows workspace");
+      // only a split (mode 3) uses a workspace: the counter region and one
+      // partial per wavefront
+      if (p.mode == 3) {
+        EXPECT(p.ws_bytes == armx::kCounterBytes + (4 * p.rows * p.segs + 255) / 256 * 256,
+               "split workspace %zu", p.ws_bytes);
+        EXPECT(p.segs >= 2 && p.segs > 0, "segs %u", p.segs);
+        EXPECT(uint64_t(p.grid) == cdiv(p.rows * p.segs, W), "split grid %d", p.grid);
+        EXPECT(uint64_t(p.grid) <= armx::kSplitMaxBlocks, "split grid %d", p.grid);
+        EXPECT(p.rows * p.segs <= armx::kSplitMaxItems, "split parts %llu",
+               (unsigned long long)(p.rows * p.segs));
+        EXPECT(c.grid_blocks <= 0 || p.grid <= c.grid_blocks, "split grid cap");
+        EXPECT(p.n > 512, "split of short rows");
+        // the same call without a workspace plans no split (fixed-order rows
+        // too long for one block's node logs are then refused)
+        Plan q;
+        const int sq = armx::make_plan(op, n, cols, ld, &c, cus, &q, false);
+        EXPECT((sq == ARMX_OK && q.mode != 3 && q.ws_bytes == 0) ||
+                   (sq == ARMX_ERR_SHAPE && op == ARMX_OP_ROWS_FIXED),
+               "split without a workspace: status %d", sq);
+      } else {
+        EXPECT(p.ws_bytes == 0, "rows workspace");
+      }
       if (p.rows == 0 || p.n == 0) continue;
       EXPECT(p.grid >= 1 && uint64_t(p.grid) <= (uint64_t(1) << 20), "rows grid %d", p.grid);
       if (p.rows > 1) EXPECT(p.ld % 8 == 0, "pitch");
@@ -183,8 +204,23 @@ int main(int argc, char** argv) {
                "MFMA-leaf short-row block %llu", (unsigned long long)(W * 64));
       }
     }
+    if (op == ARMX_OP_ROWS && p.mode == 3)
+      EXPECT(p.segs <= cdiv(p.n, 512 * R), "more segments than chains");
+    if (op == ARMX_OP_ROWS_FIXED && p.mode == 3) {
+      // aligned power-of-two ranges that cover the row, none empty
+      const uint64_t chunks = cdiv(p.n, 512), span = uint64_t(1) << p.log2_chunks;
+      EXPECT(uint64_t(p.segs) * span >= chunks && uint64_t(p.segs - 1) * span < chunks,
+             "split coverage");
+      EXPECT(p.segs <= armx::kSplitMaxSegs, "segs %u", p.segs);
+      EXPECT(p.lds_bytes + armx::kSplitMaxItems * sizeof(float) <= armx::kFixedLdsBytes,
+             "split lds");
+      EXPECT(p.lds_bytes == W * p.slots_per_wave * sizeof(float), "split lds size");
+      const uint64_t per_node = pow2(R) ? R : 1;
+      EXPECT(p.slots_per_wave % 64 == 0 && uint64_t(p.slots_per_wave) >= cdiv(span, per_node),
+             "split slots");
+    }
     if (op == ARMX_OP_ROWS_FIXED) {
-      EXPECT(pow2(W), "rows fixed W");
+      EXPECT(pow2(W) || p.mode == 3, "rows fixed W");
       if (p.mode == 1) {
         EXPECT(pow2(R) && cdiv(p.n, 512 * R) <= 64, "flat shape");
       } else if (p.mode == 0) {

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 5
+    assert armx.lib.armx_version() == 6
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
@@ -137,7 +137,8 @@ def test_mma_leaves_config_rules():
     assert armx.workspace_bytes(armx.OP_FIXED, 1 << 20, mma_leaves=True) == \
         armx.workspace_bytes(armx.OP_FIXED, 1 << 20)
     for cols in (96, 512, 520, 1 << 20):
-        assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 4, cols, mma_leaves=True) == 0
+        assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 4, cols, mma_leaves=True) == \
+            armx.workspace_bytes(armx.OP_ROWS_FIXED, 4, cols)
     # the row entry point keeps its other rules with the flag
     assert armx.lib.reduce_rows_fixed_order(FAKE, 4, 96, 96, FAKE, None, 0,
                                             cfg(mma_leaves=True, plain=True), None) == -3
@@ -209,6 +210,14 @@ def test_workspace_sizes():
     assert armx.workspace_bytes(armx.OP_SUM, 1000) == ws(1)
     assert armx.workspace_bytes(armx.OP_SUM, 0) == 0
     assert armx.workspace_bytes(armx.OP_ROWS, 4096, 65536) == 0
+    # few long rows are split over wavefronts of several blocks: the counter
+    # region + one partial per wavefront (256 CUs, R = 8: 512 wavefronts, so
+    # one row of 2^28 values in 512 parts); the pitch does not matter, so a
+    # ragged width is accepted by the query
+    assert armx.workspace_bytes(armx.OP_ROWS, 1, 1 << 28) == 256 + 4 * 512
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 1, 1 << 28) == 256 + 4 * 512
+    assert armx.workspace_bytes(armx.OP_ROWS, 4, 100_003) > 0
+    assert armx.workspace_bytes(armx.OP_ROWS, 3, 4096) == 0   # too short to split
     # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 16/8 waves -> 256 blocks
     # of 2 waves x 256 chunks (1024 threads: still one block per CU, 256
     # blocks of 16 waves x 32 chunks; 64 threads: 512 blocks of 256 chunks)
