@@ -308,6 +308,26 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     const uint64_t blocks = persistent_blocks(d, cu_count, W, R);
     const uint64_t waves = blocks * W;
     uint64_t grid;
+    // A row stream whose last round of rows is poorly filled (under 90%,
+    // within four rounds) finishes with most wavefronts idle: with a
+    // workspace, such rows are split in two instead, every half row a
+    // wavefront of its own, all resident at once when the halves fit 16
+    // per compute unit (measured on MI355X, 2^28 values: 900 rows 99.8 ->
+    // 82.1 us, 1200 rows 99.2 -> 84.8 us).
+    const uint64_t rounds = ceil_div(rows, waves);
+    if (allow_split && auto_block && rows >= waves && rows < 4 * waves &&
+        10 * rows < 9 * rounds * waves && 2 * rows <= uint64_t(kMaxWaves) * uint64_t(cu_count) &&
+        cols >= 2 * kSplitMinSegment) {
+      const uint64_t S = 2, W3 = split_block(rows * S, cu_count);
+      p.mode = 3;
+      p.waves = int(W3);
+      p.segs = unsigned(S);
+      p.grid = int(ceil_div(rows * S, W3));
+      p.partials_bytes = round_up(sizeof(float) * size_t(rows * S), 256);
+      p.ws_bytes = kCounterBytes + p.partials_bytes;
+      *plan = p;
+      return ARMX_OK;
+    }
     if (rows >= waves) {
       p.mode = 1;
       grid = blocks;
