@@ -8,18 +8,20 @@
 // at every row (rows are 16-byte aligned because ld is a multiple of 8), and
 // a row's last partial chain is masked.  Rows of at most 512 values go to
 // the segmented kernel of short_rows_kernels.hip instead.  The row's fp32
-// total is written directly -- no workspace, no second pass.  Two mappings:
+// total is written directly, except in the split mapping, where a row's parts
+// meet in a workspace and the last block adds them.  The mappings:
 //  * wave_rows: each wavefront sums whole rows (rows g, g + T, ... for
 //    wavefront g of T); the loads of the next row are issued before the
 //    current row is finished, so the pipeline runs across rows, and a row's
 //    last partial chain is masked in registers (the matrix's last row then
 //    takes exact masked loads instead); no block synchronisation at all.
 //    Used when there are many rows.
-//  * rows_split_kernel (few rows, with a workspace): every row is split over
-//    S wavefronts of several blocks, which take the row's chains
-//    round-robin as the flat sum's wavefronts take the input's, each with
-//    its own paced pipeline; each publishes its partial, and the last block
-//    to finish adds every row's S partials in index order.
+//  * rows_split_kernel (few rows, or a row stream whose last round would be
+//    poorly filled; with a workspace): every row is split over S wavefronts
+//    of several blocks, which take the row's chains round-robin as the flat
+//    sum's wavefronts take the input's, each with its own paced pipeline;
+//    each publishes its partial, and the last block to finish writes every
+//    row's balanced tree over its S partials.
 //  * otherwise each block sums a row (looping over rows if needed) and its W
 //    wavefronts take the row's chains round-robin, combined through LDS.
 #include "device_common.hpp"
