@@ -341,6 +341,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
         uint64_t S = ceil_div(waves, rows);
         S = S < cpr ? S : cpr;
         S = S < cols / kSplitMinSegment ? S : cols / kSplitMinSegment;
+        S = S < kSplitMaxSegs ? S : kSplitMaxSegs;   // what the last block's tree holds
         const uint64_t W3 = auto_block ? split_block(rows * S, cu_count) : W;
         uint64_t cap = kSplitMaxBlocks;
         if (c.grid_blocks > 0 && uint64_t(c.grid_blocks) < cap) cap = uint64_t(c.grid_blocks);

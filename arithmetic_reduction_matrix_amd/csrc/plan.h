@@ -112,17 +112,17 @@ constexpr int kShortMmaMaxBlock = 256;
 
 // Rows too few to give the persistent grid's wavefronts one row each (mode
 // 3): every row is split over several wavefronts in different blocks, each
-// publishing a partial result; one completion counter (the grid is at most
+// publishing a part; one completion counter (the grid is at most
 // kSplitMaxBlocks blocks, within what the flat sums' single-level ticket
-// takes) lets the last block stage all rows x S partials (at most
-// kSplitMaxItems) in LDS and combine every row's.  An automatic block size
-// is the part count over the compute-unit count (not a power of two), so
-// the grid keeps every compute unit busy.  Fixed order splits a row
-// into at most kSplitMaxSegs aligned power-of-two chunk ranges (the tree over
-// a row's segment roots holds 8 per lane).
-// A split pays for its completion ticket (a few microseconds) only when a
-// wavefront's share of a row without it is large: at least kSplitMinShare
-// values (64 KiB); no segment is made smaller than kSplitMinSegment values.
+// takes) lets the last block stage all rows x S parts (at most
+// kSplitMaxItems) in LDS and write every row's tree over its parts, at most
+// kSplitMaxSegs of them (8 per lane).  Fixed order cuts a row into aligned
+// power-of-two chunk ranges.  An automatic block size is the part count over
+// the compute-unit count, rounded up (not a power of two), so no compute unit
+// gets a second block.  A split pays for its completion ticket (a few
+// microseconds) only when a wavefront's share of a row without it is large:
+// at least kSplitMinShare values (64 KiB); no segment is made smaller than
+// kSplitMinSegment values.
 constexpr uint64_t kSplitMaxBlocks = 512;
 constexpr uint64_t kSplitMaxItems = 8192;
 static_assert(kSplitMaxItems == kSplitMaxBlocks * kMaxWaves, "a split grid's parts fit the stage");

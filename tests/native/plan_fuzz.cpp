@@ -168,7 +168,7 @@ int main(int argc, char** argv) {
       if (p.mode == 3) {
         EXPECT(p.ws_bytes == armx::kCounterBytes + (4 * p.rows * p.segs + 255) / 256 * 256,
                "split workspace %zu", p.ws_bytes);
-        EXPECT(p.segs >= 2 && p.segs > 0, "segs %u", p.segs);
+        EXPECT(p.segs >= 2 && p.segs <= armx::kSplitMaxSegs, "segs %u", p.segs);
         EXPECT(uint64_t(p.grid) == cdiv(p.rows * p.segs, W), "split grid %d", p.grid);
         EXPECT(uint64_t(p.grid) <= armx::kSplitMaxBlocks, "split grid %d", p.grid);
         EXPECT(p.rows * p.segs <= armx::kSplitMaxItems, "split parts %llu",

@@ -12,7 +12,9 @@ values are closed forms:
   short rows   2^26 + 1 rows of 60 values at pitch 64 (the pitch padding also
                ones): 60 per row, 120 for the last row (twos);
   ragged rows  4294968 rows of 1000 values (past 2^32 values): 1000 per row,
-               2000 for the last row (twos)."""
+               2000 for the last row (twos);
+  one row      the whole input as one row, split over many blocks: the flat
+               sums' closed forms."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +55,20 @@ def test_free_order_and_levels_past_2p32(big):
     exact = ExactSum(want << 24, want << 24, N)
     for cfg in (dict(), dict(plain=True), dict(mma_levels=True), dict(chain_r=3, block_threads=1024)):
         check_free_order(armx.reduce_sum(big, **cfg).item(), exact, str(cfg))
+
+
+def test_one_row_past_2p32_split(big):
+    # the whole input as one row: split over wavefronts of many blocks (the
+    # same closed forms as the flat sums)
+    row = big.view(1, N)
+    assert armx.workspace_bytes(armx.OP_ROWS, 1, N) > 0
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 1, N) > 0
+    assert armx.reduce_rows_fixed_order(row).item() == float((1 << 32) + 8192)
+    assert armx.reduce_rows_fixed_order(row, mma_leaves=True).item() == float((1 << 32) + 8192)
+    want = (1 << 32) + 2 * TAIL
+    exact = ExactSum(want << 24, want << 24, N)
+    for cfg in (dict(), dict(plain=True)):
+        check_free_order(armx.reduce_rows(row, **cfg).item(), exact, str(cfg))
 
 
 def test_rows_past_2p32():

@@ -47,8 +47,12 @@ def no_workspace(fn, xd, **cfg):
     return out.cpu().numpy()
 
 
-SHAPES = [(1, 1 << 20), (1, (1 << 20) + 777), (2, 300_001), (3, 1 << 18), (5, 200_000),
-          (8, 131_072 + 4096 + 13), (31, 65_536 + 5), (64, 40_000), (100, 66_000)]
+# (1, 6_297_088): 12299 chunks, R = 7 (1024 wavefronts would be 768 parts):
+# more parts than the last block's tree over a row holds unless the plan caps
+# them
+SHAPES = [(1, 1 << 20), (1, (1 << 20) + 777), (1, 6_297_088), (2, 300_001), (3, 1 << 18),
+          (5, 200_000), (8, 131_072 + 4096 + 13), (31, 65_536 + 5), (64, 40_000),
+          (100, 66_000)]
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)
