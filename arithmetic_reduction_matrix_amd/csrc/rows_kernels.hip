@@ -267,7 +267,8 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
   if (plan.mode == 3) {
     const void* fn = rows_split_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
                                            (plan.flags & ARMX_FLAG_PLAIN) != 0);
-    if (!fn || !ws || plan.segs > kSplitMaxSegs) return hipErrorInvalidValue;
+    if (!fn || !ws || plan.segs > kSplitMaxSegs || plan.rows * plan.segs > kSplitMaxItems)
+      return hipErrorInvalidValue;   // more parts than the last block's stage and tree hold
     const uint16_t* xh = static_cast<const uint16_t*>(x);
     uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
     unsigned segs = plan.segs;
