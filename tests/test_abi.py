@@ -176,6 +176,23 @@ def test_rows_argument_errors():
     assert f(None, 0, 100, 104, None, None, 0, None, None) == 0
 
 
+@pytest.mark.parametrize("fn", ["reduce_rows", "reduce_rows_fixed_order"])
+def test_rows_split_workspace_errors(fn):
+    # one row of 2^28 values is split over blocks: with a workspace it must be
+    # 256-byte aligned and large enough (checked before anything is enqueued;
+    # with ws NULL the call plans no split instead, which this host cannot run)
+    f = getattr(armx.lib, fn)
+    op = armx.OP_ROWS if fn == "reduce_rows" else armx.OP_ROWS_FIXED
+    n = 1 << 28
+    need = armx.workspace_bytes(op, 1, n)
+    assert need > 0
+    ws = 1 << 24
+    assert f(FAKE, 1, n, n, FAKE, ws + 4, need, None, None) == -2         # misaligned
+    assert f(FAKE, 1, n, n, FAKE, ws, need - 1, None, None) == -4         # too small
+    # a pitch is irrelevant to the size: a padded second row needs the same
+    assert armx.workspace_bytes(op, 2, n - 8) == armx.workspace_bytes(op, 2, n - 5)
+
+
 def test_rows_fixed_argument_errors():
     f = armx.lib.reduce_rows_fixed_order
     assert f(FAKE, 4, 100, 104, None, None, 0, None, None) == -1      # out NULL
