@@ -2,7 +2,9 @@
 guard bands filled with a pattern; after each entry point runs (at sizes with
 ragged tails, several blocks and both ticket levels), the guards must be
 intact, the workspace's counter region must be back at zero, and the part of
-the workspace past what armx_workspace_bytes asks for must be untouched."""
+the workspace past what armx_workspace_bytes asks for must be untouched (also
+for few long rows, which the row entry points split over blocks with a
+workspace)."""
 import pytest
 import torch
 
@@ -87,3 +89,27 @@ def test_row_entry_points_stay_in_bounds(rows, cols, fixed_order):
     fn(m, out=out.body(torch.float32))
     torch.cuda.synchronize()
     assert out.guards_intact(), (rows, cols, fixed_order)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, (1 << 22) + 13), (5, 200_000), (100, 66_000)])
+@pytest.mark.parametrize("fixed_order,mma_leaves", [(False, False), (True, False), (True, True)])
+def test_split_rows_stay_in_bounds(rows, cols, fixed_order, mma_leaves):
+    # few long rows split over blocks (a workspace): guards intact, counter
+    # region back at zero, the workspace tail untouched, over two calls
+    op = armx.OP_ROWS_FIXED if fixed_order else armx.OP_ROWS
+    cfg = dict(mma_leaves=True) if mma_leaves else {}
+    need = armx.workspace_bytes(op, rows, cols, **cfg)
+    assert need > 0
+    ld = (cols + 7) // 8 * 8
+    m = to_dev(si.generate_rows("normal", rows, ld, seed=rows))[:, :cols]
+    ws = Guarded(need + 1024, fill=0)
+    ws.body()[need:] = PATTERN
+    out = Guarded(4 * rows)
+    fn = armx.reduce_rows_fixed_order if fixed_order else armx.reduce_rows
+    first = fn(m, out=out.body(torch.float32), workspace=ws.body()[:need], **cfg).clone()
+    second = fn(m, out=out.body(torch.float32), workspace=ws.body()[:need], **cfg)
+    torch.cuda.synchronize()
+    assert torch.equal(first, second)
+    assert out.guards_intact() and ws.guards_intact(), (rows, cols)
+    assert bool((ws.body()[need:] == PATTERN).all().item()), (rows, cols, "workspace tail")
+    assert int(ws.body()[:256].count_nonzero().item()) == 0, (rows, cols, "counter region")
