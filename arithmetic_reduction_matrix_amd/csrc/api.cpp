@@ -74,11 +74,12 @@ int prepare_flat(int op, const void* x, size_t n, float* out, void* ws, size_t w
   return check_ws(*plan, ws, ws_bytes);
 }
 
-// Common checks and planning of the two row entry points.  The plan may split
-// few rows over wavefronts of several blocks (mode 3), which needs the
-// workspace; without one (ws NULL) it is made again without that mode.
+// Common checks and planning of the two row entry points.  The plans may
+// split few long rows, or the last round of a row stream, over wavefronts of
+// several blocks, which needs the workspace; without one (ws NULL) they are
+// made without splits.
 int prepare_rows(int op, const void* x, size_t rows, size_t cols, size_t ld, float* out,
-                 void* ws, size_t ws_bytes, const armx_config* cfg, armx::Plan* plan) {
+                 void* ws, size_t ws_bytes, const armx_config* cfg, armx::RowPlans* plans) {
   if (rows > 0 && !out) return ARMX_ERR_NULL;
   if (rows > 0 && cols > 0 && !x) return ARMX_ERR_NULL;
   if (rows > 0 && cols > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
@@ -87,9 +88,28 @@ int prepare_rows(int op, const void* x, size_t rows, size_t cols, size_t ld, flo
   int st = armx::make_plan(op, rows, cols, ld, cfg, 256, &probe);
   if (st != ARMX_OK) return st;
   const int cus = rows > 0 && cols > 0 ? current_cu_count() : 256;
-  st = armx::make_plan(op, rows, cols, ld, cfg, cus, plan, ws != nullptr);
+  st = armx::make_row_plans(op, rows, cols, ld, cfg, cus, plans, ws != nullptr);
   if (st != ARMX_OK) return st;
-  return check_ws(*plan, ws, ws_bytes);
+  armx::Plan need = plans->tail_rows ? plans->tail : plans->main;
+  need.ws_bytes = plans->ws_bytes();
+  return check_ws(need, ws, ws_bytes);
+}
+
+// Launches a row call's plans: the main one on the first rows, the tail (if
+// any) on the last tail_rows rows.
+template <class Launch>
+hipError_t launch_row_plans(const armx::RowPlans& plans, const void* x, float* out, void* ws,
+                            hipStream_t stream, Launch launch) {
+  const uint64_t head = plans.main.rows;
+  hipError_t e = launch(plans.main, x, out, ws, stream);
+  if (e != hipSuccess || plans.tail_rows == 0) return e;
+  const uint16_t* tx = static_cast<const uint16_t*>(x) + head * plans.main.ld;
+  return launch(plans.tail, tx, out + head, ws, stream);
+}
+
+void log_row_plans(const char* entry, const armx::RowPlans& plans) {
+  log_plan(entry, plans.main);
+  if (plans.tail_rows) log_plan(entry, plans.tail);
 }
 
 }  // namespace
@@ -129,21 +149,23 @@ int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, vo
 
 int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out, void* ws,
                 size_t ws_bytes, const armx_config* cfg, void* stream) {
-  armx::Plan plan;
-  const int st = prepare_rows(armx::kOpRows, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plan);
+  armx::RowPlans plans;
+  const int st = prepare_rows(armx::kOpRows, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plans);
   if (st != ARMX_OK) return st;
-  log_plan("reduce_rows", plan);
-  return hip_status(armx::launch_rows(plan, x, out, ws, static_cast<hipStream_t>(stream)));
+  log_row_plans("reduce_rows", plans);
+  return hip_status(launch_row_plans(plans, x, out, ws, static_cast<hipStream_t>(stream),
+                                     armx::launch_rows));
 }
 
 int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, float* out,
                             void* ws, size_t ws_bytes, const armx_config* cfg, void* stream) {
-  armx::Plan plan;
+  armx::RowPlans plans;
   const int st =
-      prepare_rows(armx::kOpRowsFixed, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plan);
+      prepare_rows(armx::kOpRowsFixed, x, rows, cols, ld, out, ws, ws_bytes, cfg, &plans);
   if (st != ARMX_OK) return st;
-  log_plan("reduce_rows_fixed_order", plan);
-  return hip_status(armx::launch_rows_fixed(plan, x, out, ws, static_cast<hipStream_t>(stream)));
+  log_row_plans("reduce_rows_fixed_order", plans);
+  return hip_status(launch_row_plans(plans, x, out, ws, static_cast<hipStream_t>(stream),
+                                     armx::launch_rows_fixed));
 }
 
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_config* cfg) {
@@ -156,6 +178,12 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_co
   const int cus = empty ? 256 : current_cu_count();
   // the row pitch does not change the workspace; take the smallest valid one
   const size_t ld = rows_op && n_or_rows > 1 ? (cols + 7) / 8 * 8 : cols;
+  if (rows_op) {
+    armx::RowPlans plans;
+    if (armx::make_row_plans(op, n_or_rows, cols, ld, cfg, cus, &plans) != ARMX_OK)
+      return size_t(-1);
+    return plans.ws_bytes();
+  }
   if (armx::make_plan(op, n_or_rows, cols, ld, cfg, cus, &plan) != ARMX_OK) return size_t(-1);
   return plan.ws_bytes;
 }

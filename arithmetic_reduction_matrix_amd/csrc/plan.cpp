@@ -506,4 +506,37 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   return ARMX_OK;
 }
 
+int make_row_plans(int op, uint64_t rows, uint64_t cols, uint64_t ld, const armx_config* cfg,
+                   int cu_count, RowPlans* plans, bool allow_split) {
+  RowPlans r;
+  int st = make_plan(op, rows, cols, ld, cfg, cu_count, &r.main, allow_split);
+  if (st != ARMX_OK) return st;
+  const Plan& p = r.main;
+  // Measured on MI355X (2^28 values): the second launch costs 8-16 us of
+  // dispatch, ticket and latency, less than the extra round of the
+  // fixed-order stream (2100 rows 101.4 -> 86.3 us, 2049 rows 95.6 -> 87.2)
+  // but not always less than the free-order one's (4128 rows 86.3 -> 89.3),
+  // so free order keeps its stream.
+  if (allow_split && p.mode == 1 && op == kOpRowsFixed) {
+    // the stream's wavefront count, and the rows of its last round
+    const uint64_t T = uint64_t(p.grid) * uint64_t(p.waves);
+    const uint64_t rounds = (rows + T - 1) / T;
+    const uint64_t t = rows - (rounds - 1) * T;
+    if (rounds >= 2 && 4 * t < 3 * T) {
+      RowPlans s;
+      s.tail_rows = t;
+      if (make_plan(op, rows - t, cols, ld, cfg, cu_count, &s.main, true) == ARMX_OK &&
+          make_plan(op, t, cols, ld, cfg, cu_count, &s.tail, true) == ARMX_OK &&
+          s.main.mode == 1 && uint64_t(s.main.grid) * uint64_t(s.main.waves) == T &&
+          s.tail.mode == 3) {
+        s.main.stop_event = nullptr;   // the events bracket both launches
+        s.tail.start_event = nullptr;
+        r = s;
+      }
+    }
+  }
+  *plans = r;
+  return ARMX_OK;
+}
+
 }  // namespace armx

@@ -145,4 +145,20 @@ inline uint64_t level_count(uint64_t count, uint64_t r, int level) {
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
               const armx_config* cfg, int cu_count, Plan* plan, bool allow_split = true);
 
+// The launches of one row call: the main plan and, when a fixed-order row
+// stream's last round of rows would be poorly filled (under three quarters),
+// a second launch for that round's `tail_rows` rows -- the last rows of the
+// matrix -- split over the whole device, so the stream runs full rounds only.
+// Needs the split's workspace; without one (allow_split false) there is no
+// tail.
+struct RowPlans {
+  Plan main;
+  Plan tail;
+  uint64_t tail_rows = 0;
+  size_t ws_bytes() const { return tail_rows ? tail.ws_bytes : main.ws_bytes; }
+};
+
+int make_row_plans(int op, uint64_t rows, uint64_t cols, uint64_t ld, const armx_config* cfg,
+                   int cu_count, RowPlans* plans, bool allow_split = true);
+
 }  // namespace armx

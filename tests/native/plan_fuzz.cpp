@@ -162,6 +162,26 @@ int main(int argc, char** argv) {
              "slots too few");
     }
     if (op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED) {
+      // the call's plans: a stream of full rounds plus a split tail, or one plan
+      armx::RowPlans rp;
+      EXPECT(armx::make_row_plans(op, n, cols, ld, &c, cus, &rp) == ARMX_OK, "row plans");
+      if (rp.tail_rows) {
+        const uint64_t T = uint64_t(rp.main.grid) * uint64_t(rp.main.waves);
+        EXPECT(op == ARMX_OP_ROWS_FIXED, "tail for free-order rows");
+        EXPECT(rp.main.rows + rp.tail_rows == n, "tail covers the last rows");
+        EXPECT(rp.main.mode == 1 && rp.main.rows % T == 0 && rp.main.rows >= T,
+               "head of full rounds");
+        EXPECT(rp.tail.mode == 3 && 4 * rp.tail_rows < 3 * T, "split tail");
+        EXPECT(rp.ws_bytes() == rp.tail.ws_bytes && rp.main.ws_bytes == 0, "tail workspace");
+        EXPECT(rp.main.stop_event == nullptr && rp.tail.start_event == nullptr, "tail events");
+      } else {
+        EXPECT(rp.main.mode == p.mode && rp.main.grid == p.grid && rp.ws_bytes() == p.ws_bytes,
+               "one row plan");
+      }
+      armx::RowPlans rq;
+      EXPECT(armx::make_row_plans(op, n, cols, ld, &c, cus, &rq, false) != ARMX_OK ||
+                 rq.tail_rows == 0,
+             "tail without a workspace");
       EXPECT(p.ld >= p.n, "ld");
       // only a split (mode 3) uses a workspace: the counter region and one
       // partial per wavefront

@@ -170,3 +170,33 @@ def test_split_in_a_graph():
         assert np.array_equal(bits(o_fixed.cpu().numpy()), bits(fixed_tree_row_sums(pool[rep])))
         eager = armx.reduce_rows(m, workspace=ws).cpu().numpy()
         assert np.array_equal(bits(o_free.cpu().numpy()), bits(eager)), rep
+
+
+@pytest.mark.parametrize("rows,cols", [(900, 20_000), (1100, 16_400)])
+def test_stream_with_a_poor_last_round_is_split(rows, cols):
+    # more rows than the free-order stream's wavefronts, but a last round
+    # under 90% full: each row is split in two (a workspace)
+    assert armx.workspace_bytes(armx.OP_ROWS, rows, cols) > 0, "expected a split plan"
+    x = si.generate_rows("normal", rows, cols, seed=rows + cols)
+    xd = strided(x, pitch(cols))
+    got = armx.reduce_rows(xd).cpu().numpy()
+    assert np.array_equal(bits(got), bits(armx.reduce_rows(xd).cpu().numpy()))
+    unsplit = no_workspace(armx.lib.reduce_rows, xd)
+    idx = np.unique(np.linspace(0, rows - 1, 60).astype(int))
+    for r, e in zip(idx, exact_row_sums(x[idx])):
+        check_free_order(float(got[r]), e, f"row {r}")
+        check_free_order(float(unsplit[r]), e, f"unsplit row {r}")
+
+
+def test_fixed_order_tail_launch():
+    # 2049 rows: two full rounds of the fixed-order stream, then the last
+    # round's single row split over the device in a second launch
+    rows, cols = 2049, 32_768
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, rows, cols) > 0, "expected a tail plan"
+    x = si.generate_rows("uniform11", rows, cols, seed=2049)
+    xd = strided(x, cols)
+    want = bits(fixed_tree_row_sums(x))
+    assert np.array_equal(bits(armx.reduce_rows_fixed_order(xd).cpu().numpy()), want)
+    assert np.array_equal(bits(no_workspace(armx.lib.reduce_rows_fixed_order, xd)), want)
+    got = armx.reduce_rows_fixed_order(xd, mma_leaves=True).cpu().numpy()
+    assert np.array_equal(bits(got[-3:]), bits(fixed_tree_row_sums_mma_leaves(x[-3:])))
