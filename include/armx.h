@@ -171,13 +171,14 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
  * ld       row pitch in elements, ld >= cols.
  * out      device, rows binary32 values.
  * ws       device workspace (see conventions), or NULL.  When the rows are
- *          too few for the device (fewer than the wavefronts of its
- *          persistent grid) and long, armx_workspace_bytes is non-zero and,
- *          with a workspace, every row is split over several wavefronts in
- *          different blocks whose partial sums the last block to finish
- *          adds in index order; with ws NULL each such row is summed by one
- *          block instead (slower, and in another order).  Otherwise ws is
- *          not used.
+ *          too few for the device (under three quarters of the wavefronts
+ *          of its persistent grid) and long, or more but with a last round
+ *          of rows under 90% full (up to four rounds), armx_workspace_bytes
+ *          is non-zero and, with a workspace, every row is split over
+ *          several wavefronts in different blocks whose partial sums the
+ *          last block to finish combines in a fixed order; with ws NULL
+ *          those rows are summed as without a split (slower, and in another
+ *          order).  Otherwise ws is not used.
  * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  *
@@ -248,7 +249,9 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  * x, rows, cols, ld, out, ws as for reduce_rows (ld a multiple of 8 when
  * rows > 1).  With a workspace, few long rows are split into aligned
  * power-of-two chunk ranges (complete subtrees) over wavefronts of several
- * blocks, and the last block takes each row's tree over its ranges' roots:
+ * blocks, and the last block takes each row's tree over its ranges' roots;
+ * and when a row stream's last round would be under three quarters full,
+ * that round's rows are split the same way in a second launch.  Both give
  * the same bits as any other mapping.  block_threads must be a power of
  * two.  ARMX_FLAG_PLAIN, ARMX_FLAG_ONE_CHAIN and ARMX_FLAG_TWO_PASS are not
  * accepted.  Without a split (ws NULL, or enough rows), rows longer than the
