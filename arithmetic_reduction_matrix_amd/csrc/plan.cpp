@@ -2,6 +2,7 @@
 #include "plan.h"
 
 #include <cmath>
+#include <initializer_list>
 
 namespace armx {
 namespace {
@@ -104,9 +105,13 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 //    (16 wavefronts per compute unit) in blocks of 512 threads; fixed-order
 //    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
 //    short fixed-order rows R = 1 in blocks of 256.
-//  * Longer rows: the R that pads the last chain least -- 4 to 8 for free
-//    order, 2 or 4 for fixed order (R = 2 only while a row stays within the
-//    flat kernel's 64 groups) -- the larger one on a tie, default blocks.
+//  * Longer rows: the R that pads the last chain least -- 8, 5 or 4 for
+//    free order, 2 or 4 for fixed order (R = 2 only while a row stays within
+//    the flat kernel's 64 groups) -- the larger one on a tie, default blocks.
+//    Free order skips R = 6 and 7: their grids hold 3 wavefronts per compute
+//    unit, which streamed rows measurably worse (768 rows of 348712 values:
+//    97.4 us at R = 6 against 78.7 us at R = 4; over 24 row counts at 2^28
+//    values the slowest shape went from 1.24 to 1.08 times its best R).
 struct RowShape {
   uint64_t r;
   int block;
@@ -124,7 +129,7 @@ RowShape rows_auto_shape(uint64_t cols, const OpDefaults& d, bool fixed) {
     return {r, d.block};
   }
   uint64_t best = 8;
-  for (uint64_t r = 8; r >= 4; --r)
+  for (uint64_t r : {uint64_t(5), uint64_t(4)})
     if (waste(r) < waste(best)) best = r;
   return {best, d.block};
 }

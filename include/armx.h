@@ -115,7 +115,7 @@ typedef struct armx_config {
  * and blocks of 512 threads (fixed order: R = 2 or 4 and 512 threads when a
  * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
  * rows the R that leaves a row's last chain of R chunks the least padding,
- * 4 to 8 (fixed order: 2 or 4), with the default block size.  An explicit
+ * 8, 5 or 4 (fixed order: 2 or 4), with the default block size.  An explicit
  * block_threads or chain_r overrides its part, except that rows of at most
  * 512 values with ARMX_FLAG_MMA_LEAVES run blocks of at most 256 threads (a
  * larger block_threads is lowered; no row's result depends on it). */

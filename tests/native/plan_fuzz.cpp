@@ -56,7 +56,7 @@ int main(int argc, char** argv) {
         {ARMX_OP_ROWS_FIXED, 65536, 4096, 4096, 1, 0, 1, 4, 0},
         {ARMX_OP_ROWS, 4096, 65536, 65536, 1, 0, 1, 8, 0},
         {ARMX_OP_ROWS, 57344, 4608, 4608, 1, 0, 1, 5, 0},        // 9 chunks: 5 + 4
-        {ARMX_OP_ROWS, 16384, 16896, 16896, 1, 0, 1, 7, 0},      // 33 chunks: waste 2
+        {ARMX_OP_ROWS, 16384, 16896, 16896, 1, 0, 1, 5, 0},      // 33 chunks: waste 2, no R 7
         {ARMX_OP_ROWS, 4096, 65024, 65024, 1, 0, 1, 8, 0},       // 127 chunks: waste 1
         {ARMX_OP_ROWS_FIXED, 57344, 4608, 4608, 1, 0, 1, 2, 0},  // 9 chunks
         {ARMX_OP_ROWS_FIXED, 37449, 7168, 7168, 1, 0, 1, 2, 0},  // 14 chunks

@@ -47,9 +47,9 @@ def no_workspace(fn, xd, **cfg):
     return out.cpu().numpy()
 
 
-# (1, 6_297_088): 12299 chunks, R = 7 (1024 wavefronts would be 768 parts):
-# more parts than the last block's tree over a row holds unless the plan caps
-# them
+# (1, 6_297_088): 12299 chunks, R = 5, 1024 wavefronts: 768 segments of 8192
+# values, more parts than the last block's tree over a row holds unless the
+# plan caps them
 SHAPES = [(1, 1 << 20), (1, (1 << 20) + 777), (1, 6_297_088), (2, 300_001), (3, 1 << 18),
           (5, 200_000), (8, 131_072 + 4096 + 13), (31, 65_536 + 5), (64, 40_000),
           (100, 66_000)]
