@@ -292,9 +292,10 @@ def reduce_rows(x: torch.Tensor, *, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, **cfg) -> torch.Tensor:
     """float32 sum of every row of a 2-D float16 GPU tensor whose rows are
     contiguous (``x.stride(1) == 1``) with a row pitch that is a multiple of 8.
-    A workspace is used only when there are too few rows to fill the device
-    (then each row is split over several wavefronts); by default one is
-    taken from a per-stream cache."""
+    A workspace is used only when rows are split over wavefronts of several
+    blocks (too few rows to fill the device, or a row stream whose last round
+    would be poorly filled); by default one is taken from a per-stream
+    cache."""
     return _rows_call(lib.reduce_rows, OP_ROWS, x, out, workspace, _config(**cfg),
                       "reduce_rows")
 
