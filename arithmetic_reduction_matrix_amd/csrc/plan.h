@@ -142,15 +142,19 @@ inline uint64_t level_count(uint64_t count, uint64_t r, int level) {
 // compute units of the target device.  `allow_split` lets the row entry
 // points plan mode 3 (which needs a workspace).  Returns ARMX_OK or a
 // negative status; pointers are not examined here.
+// `split_in_halves` (fixed-order rows, with allow_split) plans the split with
+// two aligned ranges per row whatever the row count.
 int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
-              const armx_config* cfg, int cu_count, Plan* plan, bool allow_split = true);
+              const armx_config* cfg, int cu_count, Plan* plan, bool allow_split = true,
+              bool split_in_halves = false);
 
 // The launches of one row call: the main plan and, when a fixed-order row
 // stream's last round of rows would be poorly filled (under three quarters),
-// a second launch for that round's `tail_rows` rows -- the last rows of the
-// matrix -- split over the whole device, so the stream runs full rounds only.
-// Needs the split's workspace; without one (allow_split false) there is no
-// tail.
+// either (two rounds) one split launch with every row in two aligned ranges,
+// or a second launch for that round's `tail_rows` rows -- the last rows of
+// the matrix -- split over the whole device, so the stream runs full rounds
+// only.  Needs the split's workspace; without one (allow_split false) there
+// is neither.
 struct RowPlans {
   Plan main;
   Plan tail;

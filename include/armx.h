@@ -251,8 +251,9 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  * power-of-two chunk ranges (complete subtrees) over wavefronts of several
  * blocks, and the last block takes each row's tree over its ranges' roots;
  * and when a row stream's last round would be under three quarters full,
- * that round's rows are split the same way in a second launch.  Both give
- * the same bits as any other mapping.  block_threads must be a power of
+ * every row is split into two ranges in one launch (two rounds) or that
+ * round's rows are split the same way in a second launch (more rounds).
+ * All give the same bits as any other mapping.  block_threads must be a power of
  * two.  ARMX_FLAG_PLAIN, ARMX_FLAG_ONE_CHAIN and ARMX_FLAG_TWO_PASS are not
  * accepted.  Without a split (ws NULL, or enough rows), rows longer than the
  * LDS node logs allow (about 2^26 values at R = 8, 2^25 at the default

@@ -174,6 +174,13 @@ int main(int argc, char** argv) {
         EXPECT(rp.tail.mode == 3 && 4 * rp.tail_rows < 3 * T, "split tail");
         EXPECT(rp.ws_bytes() == rp.tail.ws_bytes && rp.main.ws_bytes == 0, "tail workspace");
         EXPECT(rp.main.stop_event == nullptr && rp.tail.start_event == nullptr, "tail events");
+      } else if (op == ARMX_OP_ROWS_FIXED && p.mode == 1 && rp.main.mode == 3) {
+        // two rounds, the second poorly filled: every row in two ranges
+        const uint64_t T = uint64_t(p.grid) * uint64_t(p.waves);
+        EXPECT(rp.main.segs == 2 && n > T && n <= 2 * T && 4 * (n - T) < 3 * T,
+               "rows in halves");
+        EXPECT(rp.main.rows == n && rp.ws_bytes() == rp.main.ws_bytes && rp.main.ws_bytes > 0,
+               "halves workspace");
       } else {
         EXPECT(rp.main.mode == p.mode && rp.main.grid == p.grid && rp.ws_bytes() == p.ws_bytes,
                "one row plan");

@@ -200,3 +200,18 @@ def test_fixed_order_tail_launch():
     assert np.array_equal(bits(no_workspace(armx.lib.reduce_rows_fixed_order, xd)), want)
     got = armx.reduce_rows_fixed_order(xd, mma_leaves=True).cpu().numpy()
     assert np.array_equal(bits(got[-3:]), bits(fixed_tree_row_sums_mma_leaves(x[-3:])))
+
+
+def test_fixed_order_two_rounds_in_halves():
+    # just past one round of the fixed-order stream, the second round poorly
+    # filled: one split launch with every row in two aligned chunk ranges
+    rows, cols = 1100, 18_000
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, rows, cols) > 0, "expected a split plan"
+    x = si.generate_rows("uniform11", rows, cols, seed=1100)
+    xd = strided(x, pitch(cols), junk=NAN16)
+    want = bits(fixed_tree_row_sums(x))
+    assert np.array_equal(bits(armx.reduce_rows_fixed_order(xd).cpu().numpy()), want)
+    assert np.array_equal(bits(no_workspace(armx.lib.reduce_rows_fixed_order, xd)), want)
+    got = armx.reduce_rows_fixed_order(xd, mma_leaves=True).cpu().numpy()
+    idx = np.unique(np.linspace(0, rows - 1, 40).astype(int))
+    assert np.array_equal(bits(got[idx]), bits(fixed_tree_row_sums_mma_leaves(x[idx])))
