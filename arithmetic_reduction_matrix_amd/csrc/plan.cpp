@@ -536,7 +536,10 @@ int make_row_plans(int op, uint64_t rows, uint64_t cols, uint64_t ld, const armx
       // which saves the second launch's dispatch and ticket (measured on
       // MI355X, 2^26 values: 1025 rows 29.6 -> 26.9 us, 1300 rows 32.0 ->
       // 27.6, 1500 rows 30.1 -> 27.3)
-      if (rounds == 2 && 2 * rows <= kSplitMaxItems) {
+      // (only while the halves are all resident, one block per compute unit:
+      // a grid larger than the unit count leaves some units two blocks)
+      if (rounds == 2 && 2 * rows <= uint64_t(kMaxWaves) * uint64_t(cu_count) &&
+          2 * rows <= kSplitMaxItems) {
         Plan h;
         if (make_plan(op, rows, cols, ld, cfg, cu_count, &h, true, true) == ARMX_OK &&
             h.mode == 3 && h.segs == 2) {

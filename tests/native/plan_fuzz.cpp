@@ -177,7 +177,8 @@ int main(int argc, char** argv) {
       } else if (op == ARMX_OP_ROWS_FIXED && p.mode == 1 && rp.main.mode == 3) {
         // two rounds, the second poorly filled: every row in two ranges
         const uint64_t T = uint64_t(p.grid) * uint64_t(p.waves);
-        EXPECT(rp.main.segs == 2 && n > T && n <= 2 * T && 4 * (n - T) < 3 * T,
+        EXPECT(rp.main.segs == 2 && n > T && n <= 2 * T && 4 * (n - T) < 3 * T &&
+                   2 * n <= uint64_t(armx::kMaxWaves) * uint64_t(cus),
                "rows in halves");
         EXPECT(rp.main.rows == n && rp.ws_bytes() == rp.main.ws_bytes && rp.main.ws_bytes > 0,
                "halves workspace");
