@@ -320,11 +320,15 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     // wavefront of its own, all resident at once when the halves fit 16
     // per compute unit (measured on MI355X, 2^28 values: 900 rows 99.8 ->
     // 82.1 us, 1200 rows 99.2 -> 84.8 us).
+    // (grid_blocks is an upper bound on the grid: a split that would need
+    // more blocks is not planned.)
     const uint64_t rounds = ceil_div(rows, waves);
+    const uint64_t W_halves = split_block(rows * 2, cu_count);
     if (allow_split && auto_block && rows >= waves && rows < 4 * waves &&
         10 * rows < 9 * rounds * waves && 2 * rows <= uint64_t(kMaxWaves) * uint64_t(cu_count) &&
-        cols >= 2 * kSplitMinSegment) {
-      const uint64_t S = 2, W3 = split_block(rows * S, cu_count);
+        cols >= 2 * kSplitMinSegment &&
+        (c.grid_blocks == 0 || ceil_div(rows * 2, W_halves) <= uint64_t(c.grid_blocks))) {
+      const uint64_t S = 2, W3 = W_halves;
       p.mode = 3;
       p.waves = int(W3);
       p.segs = unsigned(S);

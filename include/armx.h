@@ -205,19 +205,28 @@ int reduce_rows(const void* x, size_t rows, size_t cols, size_t ld, float* out,
  * round-to-nearest-even sum of its two children (leaves are x[i] widened
  * exactly to binary32).  Each group of 256 consecutive elements is a
  * complete subtree.  The result is bit-identical for every block size,
- * chain length, grid and device, and n == 0 gives +0.0.  Only binary32
- * additions are used (no MFMA and no fused multiply-add).
+ * chain length, grid and device, and n == 0 gives +0.0.  No MFMA is used.
+ * Every node is one binary32 round-to-nearest-even addition: the first
+ * level (two adjacent binary16 leaves) is computed by v_fma_mix_f32 as
+ * lo * 1.0 + hi, whose product is exact and whose single rounding is that
+ * of the binary32 sum, and every level above by v_add_f32.  This default
+ * order is defined by IEEE arithmetic alone and is the one checked against
+ * an emulation written from that definition.
  *
  * With ARMX_FLAG_MMA_LEAVES the prescribed order has tensor-core leaves (the
- * same Abstract reconstructs tensor-core arithmetic from outputs; this
- * library's reconstruction of the gfx950 MFMA is what makes such an order
- * checkable): x is cut into chunks of 512 values (the last padded with
- * -0.0), each chunk is one v_mfma_f32_16x16x32_f16 against all-ones from a
- * zero accumulator -- column j sums, in K order, values 8s .. 8s + 7 of the
- * slots s = j, j + 16, j + 32, j + 48 -- and the chunk's node is the balanced
- * tree over its 16 column sums in column order; above the chunks the
- * balanced tree as before.  It too is bit-identical for every block size,
- * chain length, grid and device.
+ * same Abstract reconstructs tensor-core arithmetic from outputs): x is cut
+ * into chunks of 512 values (the last padded with -0.0), each chunk is one
+ * v_mfma_f32_16x16x32_f16 against all-ones from a zero accumulator --
+ * column j sums, in K order, values 8s .. 8s + 7 of the slots s = j, j + 16,
+ * j + 32, j + 48 -- and the chunk's node is the balanced tree over its 16
+ * column sums in column order; above the chunks the balanced tree as
+ * before.  It is bit-identical for every block size, chain length and grid
+ * on MI355X (gfx950).  What an MFMA leaf evaluates to is not specified by
+ * any public document: this order's expected bits come from a model of the
+ * gfx950 MFMA's accumulation that was fitted to, and checked against,
+ * outputs of that hardware (oracle/mfma_model.py).  Agreement with it is
+ * agreement with a model of one chip, not with IEEE arithmetic; the default
+ * order above is the one pinned to arithmetic alone.
  *
  * x, n, out, ws, ws_bytes as for reduce_sum.  block_threads must be a power
  * of two.  ARMX_FLAG_PLAIN and ARMX_FLAG_ONE_CHAIN are not accepted.
@@ -242,7 +251,8 @@ int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws,
  *
  * With ARMX_FLAG_MMA_LEAVES every row is summed in the order with MFMA leaves
  * of reduce_sum_fixed_order instead: exactly reduce_sum_fixed_order of that
- * row alone with the flag, and batch invariant in the same way.  Rows of at
+ * row alone with the flag, and batch invariant in the same way (its expected
+ * bits rest on the same hardware-fitted model of the MFMA, see there).  Rows of at
  * most 512 values, several to a wavefront load, take one MFMA per lane block
  * with the other rows' lanes zeroed, so values never meet another row's.
  *

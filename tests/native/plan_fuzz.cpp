@@ -74,19 +74,77 @@ int main(int argc, char** argv) {
              p.mode, p.seg_log2, p.waves, p.r, p.xcd_remap);
     }
   }
+  // a grid cap is an upper bound on every plan, splits included
+  {
+    armx_config c{};
+    c.grid_blocks = 10;
+    for (int op : {ARMX_OP_ROWS, ARMX_OP_ROWS_FIXED}) {
+      for (uint64_t rows : {uint64_t(900), uint64_t(1100), uint64_t(2049), uint64_t(3)}) {
+        Plan p;
+        const int st = armx::make_plan(op, rows, 20000, 20000, &c, 256, &p);
+        EXPECT(st == ARMX_OK && p.grid <= 10, "grid cap: op %d rows %llu status %d grid %d",
+               op, (unsigned long long)rows, st, p.grid);
+        armx::RowPlans rp;
+        EXPECT(armx::make_row_plans(op, rows, 20000, 20000, &c, 256, &rp) == ARMX_OK &&
+                   rp.main.grid <= 10 && (!rp.tail_rows || rp.tail.grid <= 10),
+               "grid cap (row plans): op %d rows %llu", op, (unsigned long long)rows);
+      }
+    }
+  }
+  // Flags each operation accepts, for the draws of valid configurations.
+  auto valid_flags = [&](int op) -> unsigned {
+    switch (op) {
+      case ARMX_OP_SUM: {
+        const unsigned k = unsigned(rng() % 4);
+        if (k == 0) return ARMX_FLAG_MMA_LEVELS | unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+        return unsigned(rng() % 16);   // PLAIN, CACHED_LOADS, ONE_CHAIN, TWO_PASS
+      }
+      case ARMX_OP_FIXED:
+        return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
+               unsigned(rng() % 2) * ARMX_FLAG_TWO_PASS | unsigned(rng() % 2) * ARMX_FLAG_MMA_LEAVES;
+      case ARMX_OP_ROWS:
+        return unsigned(rng() % 2) * ARMX_FLAG_PLAIN | unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+      case ARMX_OP_ROWS_FIXED:
+        return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
+               unsigned(rng() % 2) * ARMX_FLAG_MMA_LEAVES;
+      default:
+        return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+    }
+  };
   int accepted = 0;
   for (int it = 0; it < iters; ++it) {
     const int op = int(rng() % 6);  // 5 is not an operation
     armx_config c{};
-    c.block_threads = (rng() % 4 == 0) ? 0 : int(rng() % 1200);
-    if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
-    c.chain_r = int(rng() % 10);
-    c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
-    c.flags = unsigned(rng() % 64);
-    const uint64_t n = pick_n();
-    const uint64_t cols = pick_n() % (uint64_t(1) << 30);
-    const uint64_t ld = (rng() % 2) ? cols : cols + (rng() % 64);
-    const int cus = int(1 + rng() % 512);
+    uint64_t n, cols, ld;
+    const int cus = (rng() % 2) ? 256 : int(1 + rng() % 512);
+    if (it % 2 == 0) {
+      // anything, most of it invalid
+      c.block_threads = (rng() % 4 == 0) ? 0 : int(rng() % 1200);
+      if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
+      c.chain_r = int(rng() % 10);
+      c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
+      c.flags = unsigned(rng() % 64);
+      n = pick_n();
+      cols = pick_n() % (uint64_t(1) << 30);
+      ld = (rng() % 2) ? cols : cols + (rng() % 64);
+    } else {
+      // valid configurations: automatic or power-of-two blocks, R 0..8,
+      // flags the operation accepts; row counts near 1-4 times a row
+      // stream's wavefront count, with long rows, half of the time
+      c.block_threads = (rng() % 3 == 0) ? 0 : 64 << (rng() % 5);
+      c.chain_r = int(rng() % 9);
+      c.grid_blocks = (rng() % 3 == 0) ? int(1 + rng() % 3000) : 0;
+      c.flags = valid_flags(op);
+      if ((op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED) && rng() % 2) {
+        const uint64_t T = uint64_t(cus) * (1 + rng() % 16);
+        n = T / 2 + rng() % (4 * T + 1);
+        cols = 16384 + rng() % (uint64_t(1) << 20);
+      } else {
+        n = pick_n();
+        cols = pick_n() % (uint64_t(1) << 24);
+      }
+      ld = (rng() % 2) ? cols : (cols + 7) / 8 * 8 + 8 * (rng() % 8);
+    }
     Plan p;
     const int st = armx::make_plan(op, n, cols, ld, &c, cus, &p);
     if (op == 5) {
@@ -186,6 +244,9 @@ int main(int argc, char** argv) {
         EXPECT(rp.main.mode == p.mode && rp.main.grid == p.grid && rp.ws_bytes() == p.ws_bytes,
                "one row plan");
       }
+      EXPECT(c.grid_blocks <= 0 ||
+                 (rp.main.grid <= c.grid_blocks && (!rp.tail_rows || rp.tail.grid <= c.grid_blocks)),
+             "row plans grid cap");
       armx::RowPlans rq;
       EXPECT(armx::make_row_plans(op, n, cols, ld, &c, cus, &rq, false) != ARMX_OK ||
                  rq.tail_rows == 0,

@@ -91,8 +91,20 @@ def test_row_entry_points_stay_in_bounds(rows, cols, fixed_order):
     assert out.guards_intact(), (rows, cols, fixed_order)
 
 
-@pytest.mark.parametrize("rows,cols", [(1, (1 << 22) + 13), (5, 200_000), (100, 66_000)])
-@pytest.mark.parametrize("fixed_order,mma_leaves", [(False, False), (True, False), (True, True)])
+_FEW_ROWS = [(rows, cols, fo, mm) for rows, cols in
+             [(1, (1 << 22) + 13), (5, 200_000), (100, 66_000)]
+             for fo, mm in [(False, False), (True, False), (True, True)]]
+# row streams whose last round would be poorly filled (on 256 compute units):
+# the fixed-order stream plus a split second launch over the last rows
+# (2049 x 51192), every row in two aligned ranges in one launch (1100 x
+# 18000, both fixed orders), and the free-order stream split in two halves
+# (900 x 20000)
+_LAST_ROUND = [(2049, 51192, True, False), (2049, 51192, True, True),
+               (1100, 18000, True, False), (1100, 18000, True, True),
+               (900, 20000, False, False)]
+
+
+@pytest.mark.parametrize("rows,cols,fixed_order,mma_leaves", _FEW_ROWS + _LAST_ROUND)
 def test_split_rows_stay_in_bounds(rows, cols, fixed_order, mma_leaves):
     # few long rows split over blocks (a workspace): guards intact, counter
     # region back at zero, the workspace tail untouched, over two calls
