@@ -35,7 +35,8 @@ import torch
 
 __all__ = [
     "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
-    "reduce_sum_exact", "fixed_to_int", "workspace_bytes", "ArmxError", "Config", "LIB_PATH",
+    "reduce_sum_exact", "fixed_to_int", "workspace_bytes", "launch_plan", "ArmxError", "Config",
+    "PlanInfo", "LIB_PATH",
     "OP_SUM", "OP_ROWS", "OP_FIXED", "OP_ROWS_FIXED", "OP_EXACT",
     "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS", "FLAG_MMA_LEVELS",
     "FLAG_MMA_LEAVES",
@@ -71,11 +72,20 @@ class Config(ctypes.Structure):
                 ("start_event", ctypes.c_void_p), ("stop_event", ctypes.c_void_p)]
 
 
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``armx_plan_info``."""
+
+    _fields_ = [("grid_blocks", ctypes.c_int), ("block_threads", ctypes.c_int),
+                ("chain_r", ctypes.c_int), ("waves_per_cu", ctypes.c_double),
+                ("workspace_bytes", ctypes.c_size_t), ("lds_bytes", ctypes.c_size_t),
+                ("launches", ctypes.c_int)]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with "
-            "`python -m arithmetic_reduction_matrix_amd._build` (or __graft_entry__.build())")
+            "`python arithmetic_reduction_matrix_amd/_build.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, sz, cfgp = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Config)
     lib.reduce_sum.argtypes = [vp, sz, vp, vp, sz, cfgp, vp]
@@ -92,6 +102,8 @@ def _load() -> ctypes.CDLL:
     lib.armx_status_string.restype = ctypes.c_char_p
     lib.armx_version.argtypes = []
     lib.armx_version.restype = ctypes.c_int
+    lib.armx_launch_plan.argtypes = [ctypes.c_int, sz, sz, cfgp, ctypes.POINTER(PlanInfo)]
+    lib.armx_launch_plan.restype = ctypes.c_int
     return lib
 
 
@@ -130,6 +142,17 @@ def workspace_bytes(op: int, n_or_rows: int, cols: int = 0, **cfg) -> int:
     if v == ctypes.c_size_t(-1).value:
         raise ArmxError(-3, "armx_workspace_bytes: invalid op or configuration")
     return int(v)
+
+
+def launch_plan(op: int, n_or_rows: int, cols: int = 0, **cfg) -> dict:
+    """The launch shape the matching call would use on the current device
+    (``armx_launch_plan``): grid_blocks, block_threads, chain_r,
+    waves_per_cu, workspace_bytes, lds_bytes, launches."""
+    c = _config(**cfg)
+    info = PlanInfo()
+    _check(lib.armx_launch_plan(int(op), int(n_or_rows), int(cols), ctypes.byref(c),
+                                ctypes.byref(info)), "armx_launch_plan")
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
 # Zero-filled workspaces, one per (device, stream); a call leaves its

@@ -1,7 +1,8 @@
 """Builds libarmx.so (the HIP kernels and the C entry points) for gfx950, and
 libarmx_probe.so (a plain read stream, for measurement only).
 
-Run ``python -m arithmetic_reduction_matrix_amd._build`` or call ``build()``.
+Run ``python arithmetic_reduction_matrix_amd/_build.py`` or call ``build()`` (it needs
+only the standard library, so it runs whether or not a library is built).
 Every source is compiled each time; objects go to ``_build/`` next to this
 file and the library is written to ``libarmx.so`` in this package.
 """

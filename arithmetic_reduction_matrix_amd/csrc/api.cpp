@@ -188,6 +188,52 @@ size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols, const armx_co
   return plan.ws_bytes;
 }
 
+int armx_launch_plan(int op, size_t n_or_rows, size_t cols, const armx_config* cfg,
+                     armx_plan_info* info) {
+  if (!info) return ARMX_ERR_NULL;
+  if (op != ARMX_OP_SUM && op != ARMX_OP_ROWS && op != ARMX_OP_FIXED &&
+      op != ARMX_OP_ROWS_FIXED && op != ARMX_OP_EXACT)
+    return ARMX_ERR_CONFIG;
+  const bool rows_op = op == ARMX_OP_ROWS || op == ARMX_OP_ROWS_FIXED;
+  const bool empty = n_or_rows == 0 || (rows_op && cols == 0);
+  const int cus = empty ? 256 : current_cu_count();
+  const size_t ld = rows_op && n_or_rows > 1 ? (cols + 7) / 8 * 8 : cols;
+  armx::RowPlans plans;
+  int st;
+  if (rows_op) {
+    st = armx::make_row_plans(op, n_or_rows, cols, ld, cfg, cus, &plans);
+  } else {
+    st = armx::make_plan(op, n_or_rows, cols, ld, cfg, cus, &plans.main);
+  }
+  if (st != ARMX_OK) return st;
+  const armx::Plan& p = plans.main;
+  armx_plan_info r{};
+  r.workspace_bytes = plans.ws_bytes();
+  if (rows_op && n_or_rows == 0) {
+    r.launches = 0;   // nothing to write
+  } else if (empty) {
+    r.launches = 1;   // the zero-fill kernel
+  } else {
+    r.grid_blocks = p.grid;
+    r.block_threads = p.waves * 64;
+    r.chain_r = p.r;
+    r.lds_bytes = p.lds_bytes;
+    r.waves_per_cu = double(p.grid) * double(p.waves) / double(cus);
+    r.launches = 1;
+    if (rows_op) {
+      r.launches += plans.tail_rows ? 1 : 0;
+    } else if (p.flags & ARMX_FLAG_MMA_LEVELS) {
+      for (uint64_t c = armx::level_count(p.n, uint64_t(p.r), 1); c > 1;
+           c = armx::level_count(c, uint64_t(p.r), 2))
+        ++r.launches;
+    } else if ((p.flags & ARMX_FLAG_TWO_PASS) && p.grid > 1) {
+      ++r.launches;
+    }
+  }
+  *info = r;
+  return ARMX_OK;
+}
+
 const char* armx_status_string(int status) {
   switch (status) {
     case ARMX_OK: return "ARMX_OK";
@@ -201,6 +247,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 6; }
+int armx_version(void) { return 7; }
 
 }  // extern "C"

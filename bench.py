@@ -7,15 +7,19 @@ Two copies of the input are used in turn so that no step reads data the
 previous step left in the 256 MB Infinity Cache.
 
 Prints ONE JSON line.  `value` is elements/s over the timed steps (wall clock
-between two synchronisations); `roofline.achieved` is the algorithmic bytes of
-one launch (2 bytes per element) divided by the average kernel time, measured
-with HIP events that the kernel's own dispatch stamps (hipExtLaunchKernel) on
-the stream it runs on, on every 8th step of the timed region.  `cpu_baseline` is
-the CPU oracle (exact integer sum) timed on this host; its results also give
-`check`, the errors of the headline and the 2^30 precision-stress sums.
+between two synchronisations; each step one call through the C ABI, nothing
+else in the loop); `roofline.achieved` is the algorithmic bytes of one launch
+(2 bytes per element) divided by the average kernel time, measured with HIP
+events that the kernel's own dispatch stamps (hipExtLaunchKernel) on the
+stream it runs on, in a pass of its own after the timed steps.  `cpu_baseline`
+is the CPU oracle timed on this host: the exact integer sum and the
+balanced-tree emulator, each on one thread and on all the host threads it may
+use; its results also give `check`, the errors of the headline, of every
+block size x R point of the 2^28 matrix and of the 2^30 precision-stress sums.
 `variants` times the other rows of the hot path (MFMA-free design, exact sum,
-MMA-levels form, fixed balanced-tree order, row sums, fixed-order row sums,
-one-chain-per-wavefront grids) on their own workloads.
+MMA-levels form, fixed balanced-tree order beside the free order on the same
+data, row sums, fixed-order row sums, the block size x R matrix in both grids)
+on their own workloads.
 
 `--levels-sweep` times the recursive all-MMA form (one launch per level)
 against the single-launch form over n = 2^9 .. 2^28, for the running-time
@@ -23,8 +27,7 @@ model T(n) = 5 log_{m^2}(n) of "GPU Tensor Cores for fast Arithmetic
 Reductions" (arXiv 2001.05585, Abstract), which counts levels.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-variants]
-                    [--no-cpu-baseline] [--sweep] [--levels-sweep]
-                    [--copy-calibration]
+                    [--no-cpu-baseline] [--levels-sweep] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -36,6 +39,8 @@ import os
 import re
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -178,30 +183,87 @@ def mma_levels_count(n: int, r: int) -> int:
     return k
 
 
-def cpu_baseline(x_np, budget_s: float = 12.0, stress_np=None):
-    """The exact-sum oracle on the host: whole passes over the input until
-    `budget_s` of CPU time is spent (at least one pass), then one pass over
-    the 2^30 precision-stress input if given.  Returns the record and the
-    oracle's results (the second None without the stress input)."""
+def host_threads() -> int:
+    """Threads the CPU baseline may use: the CPUs this process may run on,
+    at most 16 (a one-GPU share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x_np, xf_np, budget_s: float = 4.0, stress_np=None):
+    """The CPU oracle on this host, as it stands: oracle.exact_sum (exact
+    integer sum) over the n = 2^28 headline input and oracle.fixed_tree_sum
+    (balanced-tree emulator) over the n = 2^26 fixed-order input, each on one
+    thread and on `host_threads()` threads.  With T threads the input is cut
+    into T aligned power-of-two parts, each part run through the same oracle
+    function in a thread (numpy releases the interpreter lock in its array
+    loops), and the parts joined by the oracle (exact_sum_of_parts: integer
+    addition; tree_over_nodes: the tree continued above the parts' roots, so
+    the bits equal the one-thread result).  Each of the four legs makes whole
+    passes until `budget_s` seconds have passed (at least one).  Then one
+    pass of the exact sum over the 2^30 precision-stress input, on T threads.
+    Returns the record and the oracle's results."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        e = oracle.exact_sum(x_np)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    elements = passes * x_np.size
-    sample = f"{passes} full pass(es) of oracle.exact_sum over the n=2^28 input"
-    e_stress = None
-    if stress_np is not None:
-        e_stress = oracle.exact_sum(stress_np)
-        el = time.perf_counter() - t0
-        elements += stress_np.size
-        sample += " and one over the n=2^30 precision-stress input"
-    return {"value": elements / el, "unit": "elements/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample} ({el:.1f} s, numpy, one thread)"}, e, e_stress
+
+    T = host_threads()
+
+    def parts(x, k):
+        step = 1 << max(0, (x.size - 1).bit_length() - (k - 1).bit_length())
+        return [x[i:i + step] for i in range(0, x.size, step)]
+
+    def exact_mt(x, pool):
+        return oracle.exact_sum_of_parts(list(pool.map(oracle.exact_sum, parts(x, T))))
+
+    def tree_mt(x, pool):
+        return oracle.tree_over_nodes(list(pool.map(oracle.fixed_tree_sum, parts(x, T))))
+
+    legs = {}
+    results = {}
+    with ThreadPoolExecutor(T) as pool:
+        for name, fn, x, threads in (
+                ("exact_sum_1t", oracle.exact_sum, x_np, 1),
+                (f"exact_sum_{T}t", lambda v: exact_mt(v, pool), x_np, T),
+                ("fixed_tree_sum_1t", oracle.fixed_tree_sum, xf_np, 1),
+                (f"fixed_tree_sum_{T}t", lambda v: tree_mt(v, pool), xf_np, T)):
+            t0 = time.perf_counter()
+            passes = 0
+            while True:
+                r = fn(x)
+                passes += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s:
+                    break
+            results[name] = r
+            legs[name] = {"elements_per_s": passes * x.size / el, "threads": threads,
+                          "passes": passes, "n": int(x.size), "seconds": el}
+        e_stress = exact_mt(stress_np, pool) if stress_np is not None else None
+    e = results["exact_sum_1t"]
+    same = (results[f"exact_sum_{T}t"].q == e.q and
+            np.float32(results[f"fixed_tree_sum_{T}t"]).view(np.uint32)
+            == np.float32(results["fixed_tree_sum_1t"]).view(np.uint32))
+    head = legs[f"exact_sum_{T}t"]
+    record = {"value": head["elements_per_s"], "unit": "elements/s", "cores": T, "kind": "oracle",
+              "sample": (f"oracle.exact_sum on {T} threads, {head['passes']} whole pass(es) over "
+                         f"the n=2^28 input ({head['seconds']:.1f} s); legs: exact_sum and "
+                         "fixed_tree_sum (n=2^26 fixed-order input), 1 thread and all threads"),
+              "cpu_model": cpu_model(), "nproc": os.cpu_count(), "legs": legs,
+              "threads_agree_bitwise": bool(same)}
+    return record, e, e_stress, results["fixed_tree_sum_1t"]
 
 
 def main() -> int:
@@ -209,12 +271,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="stamp start/stop events on every k-th timed step (roofline timing)")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the block x R matrix (paper-faithful and persistent grids)")
     ap.add_argument("--levels-sweep", action="store_true",
                     help="also time the MMA-levels form against the single-launch form "
                          "over n = 2^lo .. 2^hi (level count vs time)")
@@ -231,7 +289,6 @@ def main() -> int:
               "(run with --gpus 1)", file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import arithmetic_reduction_matrix_amd as armx
@@ -250,33 +307,49 @@ def main() -> int:
     bufs.append(bufs[0].clone())
     out = torch.empty((), dtype=torch.float32, device=dev)
     ws = torch.zeros(armx.workspace_bytes(armx.OP_SUM, n), dtype=torch.uint8, device=dev)
+    head_plan = armx.launch_plan(armx.OP_SUM, n)
 
-    # Per-launch timing: HIP events stamped by the kernel's own dispatch packet
-    # (hipExtLaunchKernel), on the stream the kernel runs on, for every
-    # `event_every`-th step of the timed region (stamping costs ~4.5 us of
-    # dispatch time per launch, so stamping every step would understate the
-    # wall-clock throughput).  The handles are created before the timed region.
-    stamped = list(range(0, args.steps, args.event_every))
-    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for i in stamped}
-    for s_ev, e_ev in evs.values():
-        s_ev.record()
-        e_ev.record()
+    # The timed steps: one call through the C ABI each, its arguments
+    # marshalled once beforehand, nothing else in the loop (no events).
+    import ctypes
+    cfg_plain = armx.Config(0, 0, 0, 0, None, None)
+    stream = torch.cuda.current_stream().cuda_stream
+    call_args = [(bufs[k].data_ptr(), n, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                  ctypes.byref(cfg_plain), stream) for k in range(2)]
+    reduce_sum_c = armx.lib.reduce_sum
 
-    def step(i, ev=(None, None)):
-        armx.reduce_sum(bufs[i & 1], out=out, workspace=ws, start_event=ev[0], stop_event=ev[1])
+    def step(i):
+        st = reduce_sum_c(*call_args[i & 1])
+        if st != 0:
+            raise RuntimeError(f"reduce_sum returned {st}")
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs.get(i, (None, None)))
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    result = float(out.item())
+
+    # Per-launch timing, in a pass of its own after the timed steps: HIP
+    # events stamped by the kernel's own dispatch packet (hipExtLaunchKernel)
+    # on the stream it runs on, on every 4th of 64 back-to-back calls (a
+    # stamp adds dispatch time, so unstamped calls keep the queue full).
+    stamped = list(range(0, 64, 4))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in stamped}
+    for s_ev, e_ev in evs.values():
+        s_ev.record()
+        e_ev.record()
+    torch.cuda.synchronize()
+    for i in range(64):
+        ev = evs.get(i, (None, None))
+        armx.reduce_sum(bufs[i & 1], out=out, workspace=ws, start_event=ev[0], stop_event=ev[1])
+    torch.cuda.synchronize()
     launch_ms = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs.values())
     avg_ms = sum(launch_ms) / len(launch_ms)
-    result = float(out.item())
 
     bytes_per_launch = 2 * n
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
@@ -296,8 +369,10 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "sum of n=2^28 fp16 uniform[-1,1) seed 2 (512 MiB), fp32 result",
-            "n": n, "block_threads": 128, "chain_r": 8, "loads": "non-temporal",
-            "grid": "persistent, 2 wavefronts per CU", "final": "last-block ticket",
+            "n": n, "block_threads": head_plan["block_threads"], "chain_r": head_plan["chain_r"],
+            "loads": "non-temporal", "grid_blocks": head_plan["grid_blocks"],
+            "grid": f"persistent, {head_plan['waves_per_cu']:g} wavefronts per CU",
+            "final": "last-block ticket",
             "input_copies_rotated": 2, "device": props.name, "cus": props.multi_processor_count,
             "workspace_bytes": ws.numel(),
         },
@@ -307,7 +382,7 @@ def main() -> int:
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "sum_kernel<R=8, non-temporal, MFMA>",
+            "kernel": f"sum_kernel<R={head_plan['chain_r']}, non-temporal, MFMA>",
             "launch_ms_avg": avg_ms, "launch_ms_median": launch_ms[len(launch_ms) // 2],
             "launch_ms_p10": launch_ms[len(launch_ms) // 10],
             "launch_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
@@ -411,18 +486,27 @@ def main() -> int:
                               armx.workspace_bytes(armx.OP_FIXED, xf_np.size, mma_leaves=True)),
                           dtype=torch.uint8, device=dev)
         fout = torch.empty((), dtype=torch.float32, device=dev)
-        for key, kw in (("fixed_order_2p26", {}), ("fixed_order_mma_leaves_2p26",
-                                                   dict(mma_leaves=True))):
-            val = armx.reduce_sum_fixed_order(fbufs[0], workspace=fws, **kw).cpu().numpy()
-            g_ms = graph_timed(torch, lambda i: armx.reduce_sum_fixed_order(
-                fbufs[i & 3], out=fout, workspace=fws, **kw), 200)
-            k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: armx.reduce_sum_fixed_order(
+        # the free-order sum on the same four copies, for the fixed/free ratio
+        fws = torch.zeros(max(fws.numel(), armx.workspace_bytes(armx.OP_SUM, xf_np.size)),
+                          dtype=torch.uint8, device=dev)
+        for key, fn, kw in (("free_order_2p26", armx.reduce_sum, {}),
+                            ("fixed_order_2p26", armx.reduce_sum_fixed_order, {}),
+                            ("fixed_order_mma_leaves_2p26", armx.reduce_sum_fixed_order,
+                             dict(mma_leaves=True))):
+            val = fn(fbufs[0], workspace=fws, **kw).cpu().numpy()
+            g_ms = graph_timed(torch, lambda i: fn(fbufs[i & 3], out=fout, workspace=fws, **kw),
+                               200)
+            k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: fn(
                 fbufs[i & 3], out=fout, workspace=fws, start_event=s_ev, stop_event=e_ev, **kw))
-            e_ms, _ = event_timed(torch, lambda i: armx.reduce_sum_fixed_order(
-                fbufs[i & 3], out=fout, workspace=fws, **kw), 200)
+            e_ms, _ = event_timed(torch, lambda i: fn(fbufs[i & 3], out=fout, workspace=fws, **kw),
+                                  200)
             var[key] = {"ms": g_ms, "gbs": 2 * xf_np.size / g_ms / 1e6,
                         "timing": "graph of 200 back-to-back calls", "kernel_ms": k_ms,
                         "eager_call_ms": e_ms, "result_bits": int(val.view(np.uint32))}
+        for key in ("fixed_order_2p26", "fixed_order_mma_leaves_2p26"):
+            var[key]["vs_free_order"] = var[key]["ms"] / var["free_order_2p26"]["ms"]
+            var[key]["kernel_vs_free_order"] = (var[key]["kernel_ms"]
+                                                / var["free_order_2p26"]["kernel_ms"])
         del fbufs
 
         xr_np = si.workload("rows_4096x65536_normal")
@@ -467,6 +551,42 @@ def main() -> int:
                 ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
                 var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
             del views, vout
+
+        # The block size x R matrix at n = 2^28 (the pages' configuration
+        # study, "GPU Tensor Cores for fast Arithmetic Reductions", Abstract):
+        # blocks of 64, 256 and 1024 threads x R in {1, 2, 4, 5}, in the
+        # pages' grid (every wavefront one chain) and the persistent grid.
+        # Kernel time by dispatch stamps (a one-chain grid at small R runs for
+        # milliseconds); each point's launch shape from the library's own plan.
+        matrix = {}
+        for grid_kind in ("one_chain", "persistent"):
+            for block in (64, 256, 1024):
+                for r in (1, 2, 4, 5):
+                    kw = dict(one_chain=grid_kind == "one_chain", block_threads=block, chain_r=r)
+                    plan = armx.launch_plan(armx.OP_SUM, n, **kw)
+                    mws = torch.zeros(max(1, plan["workspace_bytes"]), dtype=torch.uint8,
+                                      device=dev)
+                    mout = torch.empty((), dtype=torch.float32, device=dev)
+                    for i in range(2):
+                        armx.reduce_sum(bufs[i & 1], out=mout, workspace=mws, **kw)
+                    iters = 6 if plan["grid_blocks"] > 8192 else 16
+                    k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: armx.reduce_sum(
+                        bufs[i & 1], out=mout, workspace=mws, start_event=s_ev, stop_event=e_ev,
+                        **kw), iters)
+                    chains = -(-n // (512 * r))
+                    waves = plan["grid_blocks"] * block // 64
+                    in_flight = r if chains <= waves else 2 * r   # the pipeline's depth
+                    matrix[f"{grid_kind}_b{block}_r{r}"] = {
+                        "kernel_ms": k_ms, "gbs": 2 * n / k_ms / 1e6,
+                        "frac": 2 * n / k_ms / 1e6 / HBM_PEAK_GBS,
+                        "grid_blocks": plan["grid_blocks"], "waves_per_cu": plan["waves_per_cu"],
+                        "loads_in_flight_per_cu": plan["waves_per_cu"] * in_flight,
+                        "result": float(mout.item())}
+                    print(f"{grid_kind}_b{block}_r{r}", f"{k_ms * 1e3:.1f} us",
+                          f"{2 * n / k_ms / 1e6:.0f} GB/s", f"grid {plan['grid_blocks']}",
+                          f"waves/CU {plan['waves_per_cu']:.2f}", file=sys.stderr, flush=True)
+                    del mws
+        var["block_r_matrix_2p28"] = matrix
         record["variants"] = var
 
     if args.copy_calibration:
@@ -477,20 +597,6 @@ def main() -> int:
         record["copy_calibration"] = {"bytes_read": 2 * n, "bytes_written": 2 * n,
                                       "launches": 5, "kernel": "torch copy_ (fp16, 512 MiB)"}
         del dst
-
-    if args.sweep:
-        sweep = {}
-        for one_chain in (True, False):
-            for block in (64, 256, 1024):
-                for r in (1, 2, 4, 5):
-                    it = 20 if one_chain else 100
-                    ms, med = event_timed(torch, lambda i: armx.reduce_sum(
-                        bufs[i & 1], one_chain=one_chain, block_threads=block, chain_r=r), it)
-                    key = f"{'one_chain' if one_chain else 'persistent'}_b{block}_r{r}"
-                    sweep[key] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
-                    print(key, f"{ms * 1e3:.1f} us", f"{2 * n / ms / 1e6:.0f} GB/s",
-                          file=sys.stderr, flush=True)
-        record["sweep"] = sweep
 
     if args.levels_sweep:
         # GPU time per call with the queue kept full: a sleep kernel holds the
@@ -545,13 +651,24 @@ def main() -> int:
         record["levels_sweep"] = lv
 
     if not args.no_cpu_baseline:
-        record["cpu_baseline"], e, e30 = cpu_baseline(x_np, stress_np=stress_np)
+        xf_cpu = si.workload("fixed_2p26_u11")
+        record["cpu_baseline"], e, e30, tree26 = cpu_baseline(x_np, xf_cpu, stress_np=stress_np)
+        del xf_cpu
         record["check"] = {"exact_sum": e.f64, "abs_err": abs(result - e.f64),
                            "rel_err": abs(result - e.f64) / abs(e.f64)}
         if "variants" in record:
+            v = record["variants"]
             want = int(np.float32(e.f32).view(np.uint32))
-            record["check"]["exact_variant_matches_oracle"] = (
-                record["variants"]["exact_2p28"]["result_bits"] == want)
+            record["check"]["exact_variant_matches_oracle"] = v["exact_2p28"]["result_bits"] == want
+            # every point of the block x R matrix against the exact sum
+            # (the 1e-5 relative gate), and fixed order against the emulator
+            errs = {k: abs(p["result"] - e.f64) / abs(e.f64)
+                    for k, p in v["block_r_matrix_2p28"].items()}
+            record["check"]["block_r_matrix_max_rel_err"] = max(errs.values())
+            record["check"]["block_r_matrix_all_within_1e-5"] = all(
+                err <= 1e-5 for err in errs.values())
+            record["check"]["fixed_order_2p26_matches_oracle"] = (
+                v["fixed_order_2p26"]["result_bits"] == int(np.float32(tree26).view(np.uint32)))
         if e30 is not None:
             p30 = record["variants"]["precision_2p30_logu"]
             record["check"]["precision_2p30_logu"] = {

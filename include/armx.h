@@ -321,10 +321,42 @@ int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, vo
 size_t armx_workspace_bytes(int op, size_t n_or_rows, size_t cols,
                             const armx_config* cfg);
 
+/*
+ * armx_launch_plan -- the launch shape the matching call would use on the
+ * current device with this configuration (the same planning as the call
+ * itself; nothing is enqueued, no device memory is touched).  Arguments as
+ * for armx_workspace_bytes; `info` is a HOST pointer that receives:
+ *   grid_blocks      blocks of the call's main (first) kernel launch
+ *   block_threads    threads per block of that launch
+ *   chain_r          16-byte loads per lane per loop step (R) of that launch
+ *   waves_per_cu     resident wavefronts per compute unit that launch asks
+ *                    for: grid_blocks * block_threads / 64 over the
+ *                    compute-unit count (0 when nothing is launched)
+ *   workspace_bytes  as armx_workspace_bytes
+ *   lds_bytes        dynamic LDS per block of that launch
+ *   launches         kernel launches the call enqueues
+ * Without a device it assumes 256 compute units.  For the row operations
+ * the plan is the one made with a workspace.  Returns ARMX_OK, or
+ * ARMX_ERR_NULL (info NULL), ARMX_ERR_CONFIG or ARMX_ERR_SHAPE as the call
+ * would.
+ */
+typedef struct armx_plan_info {
+  int grid_blocks;
+  int block_threads;
+  int chain_r;
+  double waves_per_cu;
+  size_t workspace_bytes;
+  size_t lds_bytes;
+  int launches;
+} armx_plan_info;
+
+int armx_launch_plan(int op, size_t n_or_rows, size_t cols, const armx_config* cfg,
+                     armx_plan_info* info);
+
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 6. */
+/* armx_version -- ABI version of this header: 7. */
 int armx_version(void);
 
 #ifdef __cplusplus

@@ -23,9 +23,13 @@ What it computes:
 * ``exact_sum`` / ``exact_row_sums`` -- the plain definition of the result: the
   exact real sum of the binary16 inputs, held as an integer count of 2^-24,
   rounded once (round-to-nearest-even) to binary32 or binary64.
+* ``exact_sum_of_parts`` -- the exact sum of a concatenation from its parts'
+  exact sums (integer addition is associative).
 * ``fixed_tree_sum`` / ``fixed_tree_row_sums`` -- the prescribed fixed order:
   a balanced binary tree over the inputs (padded to a power of two with -0.0),
-  every node one binary32 round-to-nearest-even addition.
+  every node one binary32 round-to-nearest-even addition.  ``tree_over_nodes``
+  continues the same tree above nodes already computed (the roots of aligned
+  subtrees).
 * ``fixed_tree_sum_mma_leaves`` / ``fixed_tree_row_sums_mma_leaves`` -- the
   prescribed order with MFMA leaves (per row for the second):
   chunks of 512 values, each one MFMA against ones from zero as reconstructed
@@ -43,14 +47,14 @@ pages, pinned to the model's own definition and to closed forms.
 """
 from .binary16 import decode_table, decode_bits, BINARY16_QUANTUM_EXP
 from .rounding import round_scaled_int, to_binary32, to_binary64
-from .exact import ExactSum, exact_sum, exact_row_sums
+from .exact import ExactSum, exact_sum, exact_row_sums, exact_sum_of_parts
 from .tree import (fixed_tree_sum, fixed_tree_row_sums, fixed_tree_sum_mma_leaves,
-                   fixed_tree_row_sums_mma_leaves)
+                   fixed_tree_row_sums_mma_leaves, tree_over_nodes)
 
 __all__ = [
     "decode_table", "decode_bits", "BINARY16_QUANTUM_EXP",
     "round_scaled_int", "to_binary32", "to_binary64",
-    "ExactSum", "exact_sum", "exact_row_sums",
+    "ExactSum", "exact_sum", "exact_row_sums", "exact_sum_of_parts",
     "fixed_tree_sum", "fixed_tree_row_sums", "fixed_tree_sum_mma_leaves",
-    "fixed_tree_row_sums_mma_leaves",
+    "fixed_tree_row_sums_mma_leaves", "tree_over_nodes",
 ]

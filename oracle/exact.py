@@ -94,6 +94,17 @@ def exact_sum(x: np.ndarray) -> ExactSum:
     return ExactSum(total, total_abs, int(bits.size), _special(n_nan, n_pinf, n_ninf))
 
 
+def exact_sum_of_parts(parts: list[ExactSum]) -> ExactSum:
+    """The exact sum of a concatenation, from the exact sums of its parts:
+    the integers add (integer addition is associative), and the non-finite
+    cases follow the same IEEE rules as within one part."""
+    parts = list(parts)
+    specials = {p.special for p in parts}
+    n_nan = int("nan" in specials)
+    return ExactSum(sum(p.q for p in parts), sum(p.a for p in parts), sum(p.n for p in parts),
+                    _special(n_nan, int("+inf" in specials), int("-inf" in specials)))
+
+
 def exact_row_sums(x: np.ndarray) -> list[ExactSum]:
     """Exact sum of every row of a 2-D binary16 array (row r: sum_c x[r, c])."""
     if x.ndim != 2 or x.dtype != np.float16:

@@ -52,6 +52,19 @@ def fixed_tree_sum(x: np.ndarray) -> np.float32:
     return level[0]
 
 
+def tree_over_nodes(nodes: np.ndarray) -> np.float32:
+    """The same balanced tree over binary32 values that are themselves nodes:
+    padded with -0.0 to a power of two, pairs added level by level.  The
+    roots of consecutive aligned subtrees of 2^k leaves (the last one
+    possibly short, since its -0.0 padding to 2^k changes nothing) are the
+    nodes of level k, so this tree over them is the root of the whole tree.
+    No values gives +0.0."""
+    nodes = np.ascontiguousarray(nodes, dtype=np.float32).reshape(-1)
+    if nodes.size == 0:
+        return np.float32(0.0)
+    return _tree_levels(_pad_pow2(nodes, nodes.size))
+
+
 def fixed_tree_row_sums(x: np.ndarray) -> np.ndarray:
     """The same tree applied to every row of a 2-D binary16 array."""
     if x.ndim != 2 or x.dtype != np.float16:

@@ -38,7 +38,15 @@ static int failures = 0;
 static int cpu_checks(void) {
   char* fake = (char*)(uintptr_t)(1u << 20); /* never dereferenced */
   armx_config bad = {96, 0, 0, 0, NULL, NULL};
-  EXPECT(armx_version() == 6);
+  EXPECT(armx_version() == 7);
+  {
+    armx_plan_info info;
+    EXPECT(armx_launch_plan(ARMX_OP_FIXED, (size_t)1 << 26, 0, NULL, &info) == ARMX_OK);
+    EXPECT(info.grid_blocks > 0 && info.block_threads == 128 && info.chain_r == 8);
+    EXPECT(info.launches == 1 && info.workspace_bytes ==
+                                     armx_workspace_bytes(ARMX_OP_FIXED, (size_t)1 << 26, 0, NULL));
+    EXPECT(armx_launch_plan(ARMX_OP_SUM, 10, 0, &bad, &info) == ARMX_ERR_CONFIG);
+  }
   EXPECT(reduce_sum(NULL, 10, (float*)fake, fake, 1 << 20, NULL, NULL) == ARMX_ERR_NULL);
   EXPECT(reduce_sum(fake + 2, 10, (float*)fake, fake, 1 << 20, NULL, NULL) == ARMX_ERR_ALIGN);
   EXPECT(reduce_sum(fake, 10, (float*)fake, fake, 1 << 20, &bad, NULL) == ARMX_ERR_CONFIG);

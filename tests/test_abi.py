@@ -25,7 +25,8 @@ def _declared_functions(header=HEADER):
 def test_header_declares_the_three_entry_points():
     names = _declared_functions()
     for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
-              "reduce_sum_exact", "armx_workspace_bytes", "armx_status_string", "armx_version"):
+              "reduce_sum_exact", "armx_workspace_bytes", "armx_status_string", "armx_version",
+              "armx_launch_plan"):
         assert f in names
 
 
@@ -36,11 +37,36 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 6
+    assert armx.lib.armx_version() == 7
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
     assert armx.lib.armx_status_string(-99).decode() == "unknown armx status"
+
+
+def test_launch_plan_reports_the_planned_shape():
+    # the 2^28 sum's default persistent grid: 2 wavefronts of R = 8 per
+    # compute unit (256 assumed without a device), one launch
+    p = armx.launch_plan(armx.OP_SUM, 1 << 28)
+    assert (p["grid_blocks"], p["block_threads"], p["chain_r"], p["launches"]) == (256, 128, 8, 1)
+    assert p["waves_per_cu"] == 2.0
+    assert p["workspace_bytes"] == armx.workspace_bytes(armx.OP_SUM, 1 << 28)
+    # the pages' grid: one chain per wavefront
+    p = armx.launch_plan(armx.OP_SUM, 1 << 28, one_chain=True, block_threads=256, chain_r=4)
+    assert p["grid_blocks"] == (1 << 28) // (512 * 4 * 4) and p["launches"] == 1
+    assert armx.launch_plan(armx.OP_SUM, 1 << 20, two_pass=True)["launches"] == 2
+    # MMA levels: one launch per level (2^28 / (512 R) values, then / (256 R) ...)
+    assert armx.launch_plan(armx.OP_SUM, 1 << 28, mma_levels=True, chain_r=8)["launches"] == 3
+    # empty inputs: the zero-fill kernel, or nothing for zero rows
+    assert armx.launch_plan(armx.OP_SUM, 0)["launches"] == 1
+    assert armx.launch_plan(armx.OP_ROWS, 0, 100)["launches"] == 0
+    assert armx.launch_plan(armx.OP_ROWS_FIXED, 10, 0)["launches"] == 1
+    # a fixed-order row stream with a poorly filled last round: a second launch
+    p = armx.launch_plan(armx.OP_ROWS_FIXED, 2049, 51192)
+    assert p["launches"] == 2 and p["workspace_bytes"] > 0
+    with pytest.raises(armx.ArmxError):
+        armx.launch_plan(armx.OP_SUM, 10, block_threads=96)
+    assert armx.lib.armx_launch_plan(0, 10, 0, None, None) == -1
 
 
 def cfg(**kw):

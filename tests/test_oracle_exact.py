@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth_inputs as si
-from oracle import exact_row_sums, exact_sum
+from oracle import exact_row_sums, exact_sum, exact_sum_of_parts
 
 
 def _brute(x16):
@@ -77,6 +77,23 @@ def test_specials_follow_ieee_addition():
     assert exact_sum(np.array([one, -inf], np.float16)).f32 == -np.inf
     assert np.isnan(exact_sum(np.array([inf, one, -inf], np.float16)).f32)
     assert exact_sum(np.array([], np.float16)).f32 == 0
+
+
+@pytest.mark.parametrize("cuts", [[0, 1000, 1000, 5000, 65536], [0, 7, 65536], [0, 65536]])
+def test_exact_sum_of_parts_equals_whole(cuts):
+    x = si.generate("bits_finite", 65536, seed=len(cuts))
+    parts = [exact_sum(x[a:b]) for a, b in zip(cuts[:-1], cuts[1:])]
+    whole, joined = exact_sum(x), exact_sum_of_parts(parts)
+    assert (joined.q, joined.a, joined.n, joined.special) == (whole.q, whole.a, whole.n, None)
+    # non-finite parts combine by the IEEE rules of one sum
+    inf, one = np.float16(np.inf), np.float16(1)
+    p_inf = exact_sum(np.array([one, inf], np.float16))
+    p_ninf = exact_sum(np.array([-inf], np.float16))
+    p_nan = exact_sum(np.array([np.float16(np.nan)], np.float16))
+    assert exact_sum_of_parts([parts[0], p_inf]).f32 == np.inf
+    assert np.isnan(exact_sum_of_parts([p_inf, parts[0], p_ninf]).f32)
+    assert np.isnan(exact_sum_of_parts([p_nan, parts[0]]).f32)
+    assert exact_sum_of_parts([]).f32 == 0
 
 
 def test_f32_worked_ties():

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import synth_inputs as si
-from oracle import exact_sum, fixed_tree_row_sums, fixed_tree_sum, to_binary32
+from oracle import exact_sum, fixed_tree_row_sums, fixed_tree_sum, to_binary32, tree_over_nodes
 
 from _golden import bits32, tree_examples
 
@@ -134,6 +134,28 @@ def test_tile_subtrees_compose():
     while level.size > 1:
         level = level[0::2] + level[1::2]
     assert bits32(level[0]) == bits32(fixed_tree_sum(x))
+
+
+@pytest.mark.parametrize("n,log2_part", [(1000, 6), (100_003, 12), (1 << 16, 16), (5, 2),
+                                         (70_000, 17)])
+def test_tree_over_nodes_continues_the_tree(n, log2_part):
+    # the roots of consecutive aligned subtrees of 2^k leaves (the last one
+    # short) are level-k nodes: the tree over them is the whole tree's root
+    x = si.generate("logu_signed", n, seed=n)
+    step = 1 << log2_part
+    roots = [fixed_tree_sum(x[i:i + step]) for i in range(0, n, step)]
+    assert bits32(tree_over_nodes(np.array(roots, np.float32))) == bits32(fixed_tree_sum(x))
+
+
+def test_tree_over_nodes_worked_example():
+    # the nodes 1, 2^-24, 2^-24, 2^-24: (1 + 2^-24) is a tie -> 1, (2^-24 +
+    # 2^-24) = 2^-23, 1 + 2^-23 exact; left to right would give 1.0
+    got = tree_over_nodes(np.array([1, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24], np.float32))
+    assert got == np.float32(1 + 2.0 ** -23)
+    # three nodes: the fourth is -0.0 padding, so +0.0 + +0.0 stays +0.0
+    assert bits32(tree_over_nodes(np.array([0.0, 0.0, 0.0], np.float32))) == 0
+    assert bits32(tree_over_nodes(np.array([-0.0, -0.0, -0.0], np.float32))) == 0x80000000
+    assert bits32(tree_over_nodes(np.array([], np.float32))) == 0
 
 
 def test_specials():
