@@ -11,6 +11,8 @@
 
 #include <cstdint>
 
+#include "armx.h"
+
 namespace armx {
 namespace dev {
 
@@ -212,6 +214,23 @@ __device__ __forceinline__ floatx4 mfma_ones(floatx4 acc, u32x4 tile) {
                                                 0, 0);
 }
 
+// The signed ones operand: A = 16 x 32 with rows 0-7 all +1 and rows 8-15 all
+// -1.  Lane l supplies row l % 16 of A, so lanes with l % 16 >= 8 hold -1.
+// Output row i of D = C + A * T then accumulates +(column sum) for i < 8 and
+// -(column sum) for i >= 8; lane l holds rows 4 (l / 16) .. 4 (l / 16) + 3,
+// so lanes 0-31 accumulate the + sums and lanes 32-63 the - sums of the
+// same 16 columns, each output element on its own.  Products by -1.0 are
+// exact, so the - elements are the same accumulations of the negated values.
+__device__ __forceinline__ half8 signed_ones_operand() {
+  const _Float16 s = (lane_id() & 8) ? _Float16(-1) : _Float16(1);
+  return half8{s, s, s, s, s, s, s, s};
+}
+
+__device__ __forceinline__ floatx4 mfma_signed(floatx4 acc, u32x4 tile, half8 a) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8, tile), acc, 0, 0,
+                                                0);
+}
+
 // Sum of one 16-byte load's 8 values, converted and added in fp32 (the
 // MFMA-free design).
 __device__ __forceinline__ void plain_add8(float& a, float& b, u32x4 t) {
@@ -255,32 +274,61 @@ __device__ __forceinline__ void load_chain(const u32x4* __restrict__ base, uint6
   for (int r = 0; r < R; ++r) v[r] = load16<NT>(p + r * 64);
 }
 
+// Designs of the free-order chain step (the template parameter D):
+//   kSigned  MFMA against the signed ones operand (the default): lanes 0-31
+//            carry the + column sums, lanes 32-63 the - column sums, and the
+//            wavefront total is half their difference.  The MFMA's
+//            accumulation cuts low bits toward minus infinity in some steps
+//            (measured on gfx950), which leans a + sum low and a - sum high
+//            by the same amount in distribution, so the difference cancels
+//            the lean; at no extra instruction per load.
+//   kPlain   the MFMA-free design: per-lane binary16 -> binary32 and fp32 adds.
+//   kOnes    MFMA against the all-ones operand, every lane a + column sum
+//            (the literal form; its results lean low on data of wide range).
+constexpr int kSigned = 0;
+constexpr int kPlain = 1;
+constexpr int kOnes = 2;
+
+// The design a call's flags select.
+inline int chain_design(unsigned flags) {
+  if (flags & ARMX_FLAG_PLAIN) return kPlain;
+  if (flags & ARMX_FLAG_ALL_ONES) return kOnes;
+  return kSigned;
+}
+
 // One chain: R tile steps whose fp32 result starts from zero; the caller adds
 // it (one round-to-nearest-even v_add_f32) into the running per-lane sum.
 // Keeping each chain's sub-result separate is what holds the error down: a
 // single accumulator carried across many MFMAs grows large, and the MFMA's
 // own accumulation then loses low bits on every step.
-//   MFMA design: lane l's chain value is the sum of column l % 16 of the R
-//   tiles (the same value in all four accumulator registers).
+//   MFMA designs: lane l's chain value is the sum of column l % 16 of the R
+//   tiles (kSigned: negated in lanes 32-63; the same value in all four
+//   accumulator registers).
 //   MFMA-free design: lane l's chain value is the sum of its own 8 R values.
-template <int R, bool PLAIN>
+template <int R, int D>
 __device__ __forceinline__ float chain_value(const u32x4 (&v)[R]) {
-  if constexpr (PLAIN) {
+  if constexpr (D == kPlain) {
     float a = 0.0f, b = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) plain_add8(a, b, v[r]);
     return a + b;
-  } else {
+  } else if constexpr (D == kOnes) {
     floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < R; ++r) acc = mfma_ones(acc, v[r]);
     return acc[0];
+  } else {
+    const half8 a = signed_ones_operand();
+    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc = mfma_signed(acc, v[r], a);
+    return acc[0];
   }
 }
 
-template <int R, bool PLAIN>
+template <int R, int D>
 __device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
-  run += chain_value<R, PLAIN>(v);
+  run += chain_value<R, D>(v);
 }
 
 // Accumulates the full chains c0, c0 + stride, ..., (`iters` of them).
@@ -293,7 +341,7 @@ __device__ __forceinline__ void chain_step(const u32x4 (&v)[R], float& run) {
 // value is added into `run` one half-step later, after the next loads are
 // issued, so the wait for the MFMA chain's result never delays a prefetch.
 // PACE > 0 pauses after every chain (pace_pause).
-template <int R, bool NT, bool PLAIN, int PACE = 0>
+template <int R, bool NT, int D, int PACE = 0>
 __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, uint64_t c0,
                                               uint64_t iters, uint64_t stride, int lane,
                                               float& run) {
@@ -303,7 +351,7 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
     // chain is not loaded again while its first load is still in flight
     u32x4 v[R];
     load_chain<R, NT>(base, c0, lane, v);
-    run += chain_value<R, PLAIN>(v);
+    run += chain_value<R, D>(v);
     return;
   }
   const uint64_t last = c0 + (iters - 1) * stride;
@@ -314,13 +362,13 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
     load_chain<R, NT>(base, j + 1 < iters ? c0 + (j + 1) * stride : last, lane, b);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
     run += pending;
-    pending = chain_value<R, PLAIN>(a);
+    pending = chain_value<R, D>(a);
     pace_pause<PACE>();
     load_chain<R, NT>(base, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, a);
     __builtin_amdgcn_sched_barrier(0);
     if (j + 1 < iters) {
       run += pending;
-      pending = chain_value<R, PLAIN>(b);
+      pending = chain_value<R, D>(b);
     }
     pace_pause<PACE>();
   }
@@ -329,7 +377,7 @@ __device__ __forceinline__ void stream_chains(const u32x4* __restrict__ base, ui
 
 // The partial chain c (elements [c R 512, end) of a segment of `len` values
 // starting at xh); values past `len` count as +0.0.
-template <int R, bool PLAIN>
+template <int R, int D>
 __device__ __forceinline__ void tail_chain(const uint16_t* __restrict__ xh, uint64_t c,
                                            uint64_t len, int lane, float& run) {
   u32x4 v[R];
@@ -338,7 +386,7 @@ __device__ __forceinline__ void tail_chain(const uint16_t* __restrict__ xh, uint
     const uint64_t e = (c * R + r) * 512 + uint64_t(lane) * 8;
     v[r] = e < len ? load8_masked(xh, e, len, 0u) : u32x4{0u, 0u, 0u, 0u};
   }
-  chain_step<R, PLAIN>(v, run);
+  chain_step<R, D>(v, run);
 }
 
 // ---- rows that end inside a chain --------------------------------------------
@@ -412,13 +460,21 @@ __device__ __forceinline__ void mask_row_chain(u32x4 (&v)[R], uint64_t c, uint64
 }
 
 // The wavefront total of the running per-lane sums (valid in every lane).
-template <bool PLAIN>
+template <int D>
 __device__ __forceinline__ float wave_total(float run) {
-  if constexpr (PLAIN) {
+  if constexpr (D == kPlain) {
     return wave_sum(run);
-  } else {
+  } else if constexpr (D == kOnes) {
     // lanes 0..15 hold the 16 column totals (lanes 16..63 repeat them)
     return row16_sum(run);
+  } else {
+    // every 16-lane row sums its 16 columns: rows 0-1 (lanes 0-31) hold P,
+    // the + total, rows 2-3 hold N, the - total; the total is (P - N) / 2
+    // (one rounding; the halving is exact)
+    const float t = row16_sum(run);
+    const float p = bitsf(__builtin_amdgcn_readlane(fbits(t), 0));
+    const float m = bitsf(__builtin_amdgcn_readlane(fbits(t), 32));
+    return (p - m) * 0.5f;
   }
 }
 

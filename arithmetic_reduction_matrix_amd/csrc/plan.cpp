@@ -9,7 +9,8 @@ namespace {
 
 constexpr unsigned kKnownFlags = ARMX_FLAG_PLAIN | ARMX_FLAG_CACHED_LOADS |
                                  ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS |
-                                 ARMX_FLAG_MMA_LEVELS | ARMX_FLAG_MMA_LEAVES;
+                                 ARMX_FLAG_MMA_LEVELS | ARMX_FLAG_MMA_LEAVES |
+                                 ARMX_FLAG_ALL_ONES;
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
@@ -199,6 +200,11 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
 
   if (op != kOpSum && (c.flags & ARMX_FLAG_MMA_LEVELS)) return ARMX_ERR_CONFIG;
   if (op != kOpFixed && op != kOpRowsFixed && (c.flags & ARMX_FLAG_MMA_LEAVES))
+    return ARMX_ERR_CONFIG;
+  // the all-ones operand is a choice of the free-order MFMA design only
+  if ((c.flags & ARMX_FLAG_ALL_ONES) &&
+      ((op != kOpSum && op != kOpRows) ||
+       (c.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_MMA_LEVELS))))
     return ARMX_ERR_CONFIG;
   if (op == kOpExact) {
     // persistent grid as for the free-order sum; only the load kind is a flag

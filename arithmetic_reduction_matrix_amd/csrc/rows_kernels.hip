@@ -2,9 +2,10 @@
 //
 // Many independent sums of the kind in "GPU Tensor Cores for fast Arithmetic
 // Reductions" (arXiv 2001.05585), Abstract, one per row.  Every chunk of a
-// row goes through one v_mfma_f32_16x16x32_f16 against all-ones (or, with
-// ARMX_FLAG_PLAIN, per-lane fp32 adds) and R of them chain into the fp32
-// accumulators.  A chunk never straddles two rows: the chunk grid restarts
+// row goes through one v_mfma_f32_16x16x32_f16 against the signed ones
+// operand (or all ones with ARMX_FLAG_ALL_ONES; or, with ARMX_FLAG_PLAIN,
+// per-lane fp32 adds; the designs of device_common.hpp) and R of them chain
+// into the fp32 accumulators.  A chunk never straddles two rows: the chunk grid restarts
 // at every row (rows are 16-byte aligned because ld is a multiple of 8), and
 // a row's last partial chain is masked.  Rows of at most 512 values go to
 // the segmented kernel of short_rows_kernels.hip instead.  The row's fp32
@@ -51,7 +52,7 @@ struct RowCursor {
 // partial chain, read and masked as load_row_chain and mask_row_chain
 // describe (values past the row count as +0.0).  At the end of a row its
 // total is written and the running sum restarts.
-template <int R, bool NT, bool PLAIN>
+template <int R, bool NT, int D>
 __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                           uint64_t cols, uint64_t ld, float* __restrict__ out,
                                           uint64_t g, uint64_t T, int lane) {
@@ -86,7 +87,7 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
     run += pending;
     have_pending = false;
     if (pr.c + 1 == cpr) {
-      const float total = wave_total<PLAIN>(run);
+      const float total = wave_total<D>(run);
       if (lane == 0) out[g + pr.k * T] = total;
       run = 0.0f;
     }
@@ -95,7 +96,7 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
   auto reduce = [&](u32x4 (&v)[R]) {
     retire();
     if (partial && rd.c + 1 == cpr) mask_row_chain<R>(v, rd.c, cols, 0u, lane);
-    pending = chain_value<R, PLAIN>(v);
+    pending = chain_value<R, D>(v);
     have_pending = true;
     rd.next(cpr);
   };
@@ -114,17 +115,17 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
 
 // One row summed by one wavefront with exact masked loads (no read past
 // the row): its whole chains pipelined, then the partial chain.
-template <int R, bool NT, bool PLAIN>
+template <int R, bool NT, int D>
 __device__ __forceinline__ float row_total_masked(const uint16_t* __restrict__ xr, uint64_t cols,
                                                   int lane) {
   const uint64_t chains_full = cols / (uint64_t(R) * 512);
   float run = 0.0f;
-  stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane, run);
-  if (chains_full * R * 512 < cols) tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
-  return wave_total<PLAIN>(run);
+  stream_chains<R, NT, D>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane, run);
+  if (chains_full * R * 512 < cols) tail_chain<R, D>(xr, chains_full, cols, lane, run);
+  return wave_total<D>(run);
 }
 
-template <int R, bool NT, bool PLAIN>
+template <int R, bool NT, int D>
 __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__ x, uint64_t rows,
                                                     uint64_t cols, uint64_t ld,
                                                     float* __restrict__ out, int wave_rows,
@@ -140,9 +141,9 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
     const uint64_t T = uint64_t(gridDim.x) * W;
     // the last row stays out of the stream when rows end inside a chain
     const uint64_t streamed = tail ? rows - 1 : rows;
-    rows_flat<R, NT, PLAIN>(x, streamed, cols, ld, out, g, T, lane);
+    rows_flat<R, NT, D>(x, streamed, cols, ld, out, g, T, lane);
     if (tail && g == (rows - 1) % T) {
-      const float total = row_total_masked<R, NT, PLAIN>(x + (rows - 1) * ld, cols, lane);
+      const float total = row_total_masked<R, NT, D>(x + (rows - 1) * ld, cols, lane);
       if (lane == 0) out[rows - 1] = total;
     }
     return;
@@ -153,9 +154,9 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
     float run = 0.0f;
     const uint64_t c = uint64_t(wave_id());
     const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / W + 1 : 0;
-    stream_chains<R, NT, PLAIN>(reinterpret_cast<const u32x4*>(xr), c, iters, W, lane, run);
-    if (tail && c + iters * W == chains_full) tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
-    const float total = block_sum_lane0(wave_total<PLAIN>(run), red);
+    stream_chains<R, NT, D>(reinterpret_cast<const u32x4*>(xr), c, iters, W, lane, run);
+    if (tail && c + iters * W == chains_full) tail_chain<R, D>(xr, chains_full, cols, lane, run);
+    const float total = block_sum_lane0(wave_total<D>(run), red);
     if (threadIdx.x == 0) out[row] = total;
   }
 }
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
 // block writes out[r] = the balanced tree over row r's S partials in index
 // order (combine_split_rows), so the result depends on the configuration
 // only.
-template <int R, bool NT, bool PLAIN>
+template <int R, bool NT, int D>
 __global__ __launch_bounds__(1024) void rows_split_kernel(const uint16_t* __restrict__ x,
                                                           uint64_t rows, uint64_t cols,
                                                           uint64_t ld, float* __restrict__ out,
@@ -189,15 +190,15 @@ __global__ __launch_bounds__(1024) void rows_split_kernel(const uint16_t* __rest
     float run = 0.0f;
     // pacing as for the flat sum
     if (iters >= kPaceLongChains) {
-      stream_chains<R, NT, PLAIN, PLAIN ? 4 : 8>(xv, s, iters, S, lane, run);
-    } else if (!PLAIN && iters >= kPaceShortChains) {
-      stream_chains<R, NT, PLAIN, 2>(xv, s, iters, S, lane, run);
+      stream_chains<R, NT, D, D == kPlain ? 4 : 8>(xv, s, iters, S, lane, run);
+    } else if (D != kPlain && iters >= kPaceShortChains) {
+      stream_chains<R, NT, D, 2>(xv, s, iters, S, lane, run);
     } else {
-      stream_chains<R, NT, PLAIN>(xv, s, iters, S, lane, run);
+      stream_chains<R, NT, D>(xv, s, iters, S, lane, run);
     }
     if (chains_full * R * 512 < cols && s + iters * S == chains_full)
-      tail_chain<R, PLAIN>(xr, chains_full, cols, lane, run);
-    const float total = wave_total<PLAIN>(run);
+      tail_chain<R, D>(xr, chains_full, cols, lane, run);
+    const float total = wave_total<D>(run);
     if (lane == 0) __hip_atomic_store(partials + item, total, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the partial is stored
@@ -207,55 +208,47 @@ __global__ __launch_bounds__(1024) void rows_split_kernel(const uint16_t* __rest
   combine_split_rows(partials, rows, segs, out, stage);
 }
 
-template <int R, bool NT, bool PLAIN>
-const void* rows_ptr() {
-  return reinterpret_cast<const void*>(&rows_kernel<R, NT, PLAIN>);
-}
-
-template <int R>
-const void* pick_rows(bool nt, bool plain) {
-  if (nt) return plain ? rows_ptr<R, true, true>() : rows_ptr<R, true, false>();
-  return plain ? rows_ptr<R, false, true>() : rows_ptr<R, false, false>();
-}
-
-const void* rows_kernel_for(int r, bool nt, bool plain) {
-  switch (r) {
-    case 1: return pick_rows<1>(nt, plain);
-    case 2: return pick_rows<2>(nt, plain);
-    case 3: return pick_rows<3>(nt, plain);
-    case 4: return pick_rows<4>(nt, plain);
-    case 5: return pick_rows<5>(nt, plain);
-    case 6: return pick_rows<6>(nt, plain);
-    case 7: return pick_rows<7>(nt, plain);
-    case 8: return pick_rows<8>(nt, plain);
+template <template <int, bool, int> class K, int R, bool NT>
+const void* pick_design(int d) {
+  switch (d) {
+    case kSigned: return K<R, NT, kSigned>::ptr();
+    case kPlain: return K<R, NT, kPlain>::ptr();
+    case kOnes: return K<R, NT, kOnes>::ptr();
     default: return nullptr;
   }
 }
 
-template <int R, bool NT, bool PLAIN>
-const void* split_ptr() {
-  return reinterpret_cast<const void*>(&rows_split_kernel<R, NT, PLAIN>);
+template <template <int, bool, int> class K, int R>
+const void* pick_nt(bool nt, int d) {
+  return nt ? pick_design<K, R, true>(d) : pick_design<K, R, false>(d);
 }
 
-template <int R>
-const void* pick_split(bool nt, bool plain) {
-  if (nt) return plain ? split_ptr<R, true, true>() : split_ptr<R, true, false>();
-  return plain ? split_ptr<R, false, true>() : split_ptr<R, false, false>();
-}
-
-const void* rows_split_kernel_for(int r, bool nt, bool plain) {
+template <template <int, bool, int> class K>
+const void* kernel_for(int r, bool nt, int d) {
   switch (r) {
-    case 1: return pick_split<1>(nt, plain);
-    case 2: return pick_split<2>(nt, plain);
-    case 3: return pick_split<3>(nt, plain);
-    case 4: return pick_split<4>(nt, plain);
-    case 5: return pick_split<5>(nt, plain);
-    case 6: return pick_split<6>(nt, plain);
-    case 7: return pick_split<7>(nt, plain);
-    case 8: return pick_split<8>(nt, plain);
+    case 1: return pick_nt<K, 1>(nt, d);
+    case 2: return pick_nt<K, 2>(nt, d);
+    case 3: return pick_nt<K, 3>(nt, d);
+    case 4: return pick_nt<K, 4>(nt, d);
+    case 5: return pick_nt<K, 5>(nt, d);
+    case 6: return pick_nt<K, 6>(nt, d);
+    case 7: return pick_nt<K, 7>(nt, d);
+    case 8: return pick_nt<K, 8>(nt, d);
     default: return nullptr;
   }
 }
+
+template <int R, bool NT, int D>
+struct RowsK {
+  static const void* ptr() { return reinterpret_cast<const void*>(&rows_kernel<R, NT, D>); }
+};
+
+template <int R, bool NT, int D>
+struct SplitK {
+  static const void* ptr() {
+    return reinterpret_cast<const void*>(&rows_split_kernel<R, NT, D>);
+  }
+};
 
 }  // namespace
 
@@ -265,8 +258,8 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
   if (plan.n == 0) return launch_zero(out, plan.rows, stream);
   if (plan.mode == 2) return launch_short_rows(plan, x, out, stream);
   if (plan.mode == 3) {
-    const void* fn = rows_split_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
-                                           (plan.flags & ARMX_FLAG_PLAIN) != 0);
+    const void* fn = kernel_for<SplitK>(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                        chain_design(plan.flags));
     if (!fn || !ws || plan.segs > kSplitMaxSegs || plan.rows * plan.segs > kSplitMaxItems)
       return hipErrorInvalidValue;   // more parts than the last block's stage and tree hold
     const uint16_t* xh = static_cast<const uint16_t*>(x);
@@ -276,8 +269,8 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
     void* args[] = {&xh, &rows, &cols, &ld, &out, &segs, &w.counters, &w.partials};
     return launch_main(plan, fn, args, stream);
   }
-  const void* fn = rows_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
-                                   (plan.flags & ARMX_FLAG_PLAIN) != 0);
+  const void* fn = kernel_for<RowsK>(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                     chain_design(plan.flags));
   if (!fn) return hipErrorInvalidValue;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;

@@ -1,15 +1,19 @@
-// Free-order sum: chained MFMAs against an all-ones operand (and the MFMA-free
+// Free-order sum: chained MFMAs against a ones operand (and the MFMA-free
 // comparison design).
 //
 // "GPU Tensor Cores for fast Arithmetic Reductions" (arXiv 2001.05585),
 // Abstract: the sum of n numbers is encoded as chains of m x m
 // matrix-multiply-accumulates, each chain of R kept as a 32-bit float, and all
 // chain results are reduced into one 32-bit float.  On gfx950 one chain step
-// is v_mfma_f32_16x16x32_f16 with A = ones(16x32) and B = the 32 x 16 tile a
-// wavefront brings in with one 16-byte load per lane; R of them accumulate
-// into the same fp32 registers.  The MFMA-free design ("conventional"
-// reduction of the same Abstract) converts every value and adds it in fp32
-// per lane.
+// is v_mfma_f32_16x16x32_f16 with A = a 16 x 32 matrix of ones and B = the
+// 32 x 16 tile a wavefront brings in with one 16-byte load per lane; R of
+// them accumulate into the same fp32 registers.  By default A's lower 8 rows
+// are -1 (the signed design, kSigned in device_common.hpp): half the
+// accumulator elements carry the column sums and half their negations, and
+// the total is half the difference, which cancels the downward lean of the
+// MFMA's accumulation on wide-range data; ARMX_FLAG_ALL_ONES keeps A all
+// ones.  The MFMA-free design ("conventional" reduction of the same Abstract)
+// converts every value and adds it in fp32 per lane.
 //
 // Precision: every chain's R tile steps start from a zero fp32 accumulator,
 // and the chain result is then added into a running fp32 sum, so the MFMA
@@ -42,7 +46,7 @@ __device__ float reduce_partials(const float* partials, unsigned count, float* r
   return block_sum_lane0(s, red);
 }
 
-template <int R, bool NT, bool PLAIN>
+template <int R, bool NT, int D>
 __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, uint64_t n,
                                                    uint64_t chains_full,
                                                    unsigned* __restrict__ counters,
@@ -59,21 +63,22 @@ __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, 
 
   float run = 0.0f;
   const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
-  // pacing (pace_pause), measured on MI355X: MFMA design 8 from 64 chains per
-  // wavefront, 2 from 8; MFMA-free design 4 from 64 chains
+  // pacing (pace_pause), measured on MI355X: MFMA designs 8 from 64 chains
+  // per wavefront, 2 from 8; MFMA-free design 4 from 64 chains
+  constexpr bool PLAIN = D == kPlain;
   if (iters >= kPaceLongChains) {
-    stream_chains<R, NT, PLAIN, PLAIN ? 4 : 8>(x, c, iters, total_waves, lane, run);
+    stream_chains<R, NT, D, PLAIN ? 4 : 8>(x, c, iters, total_waves, lane, run);
   } else if (!PLAIN && iters >= kPaceShortChains) {
-    stream_chains<R, NT, PLAIN, 2>(x, c, iters, total_waves, lane, run);
+    stream_chains<R, NT, D, 2>(x, c, iters, total_waves, lane, run);
   } else {
-    stream_chains<R, NT, PLAIN>(x, c, iters, total_waves, lane, run);
+    stream_chains<R, NT, D>(x, c, iters, total_waves, lane, run);
   }
   c += iters * total_waves;
   if (c == chains_full && chains_full * R * 512 < n) {
     // the partial chain at the end: values past n read as +0.0
-    tail_chain<R, PLAIN>(reinterpret_cast<const uint16_t*>(x), c, n, lane, run);
+    tail_chain<R, D>(reinterpret_cast<const uint16_t*>(x), c, n, lane, run);
   }
-  const float block_total = block_sum_lane0(wave_total<PLAIN>(run), red);
+  const float block_total = block_sum_lane0(wave_total<D>(run), red);
 
   if (gridDim.x == 1) {
     if (threadIdx.x == 0) out[0] = block_total;
@@ -100,27 +105,31 @@ __global__ void zero_kernel(float* out, uint64_t count) {
   if (i < count) out[i] = 0.0f;
 }
 
-template <int R, bool NT, bool PLAIN>
-const void* sum_kernel_ptr() {
-  return reinterpret_cast<const void*>(&sum_kernel<R, NT, PLAIN>);
+template <int R, bool NT>
+const void* pick_design(int d) {
+  switch (d) {
+    case kSigned: return reinterpret_cast<const void*>(&sum_kernel<R, NT, kSigned>);
+    case kPlain: return reinterpret_cast<const void*>(&sum_kernel<R, NT, kPlain>);
+    case kOnes: return reinterpret_cast<const void*>(&sum_kernel<R, NT, kOnes>);
+    default: return nullptr;
+  }
 }
 
 template <int R>
-const void* pick_sum(bool nt, bool plain) {
-  if (nt) return plain ? sum_kernel_ptr<R, true, true>() : sum_kernel_ptr<R, true, false>();
-  return plain ? sum_kernel_ptr<R, false, true>() : sum_kernel_ptr<R, false, false>();
+const void* pick_sum(bool nt, int d) {
+  return nt ? pick_design<R, true>(d) : pick_design<R, false>(d);
 }
 
-const void* sum_kernel_for(int r, bool nt, bool plain) {
+const void* sum_kernel_for(int r, bool nt, int d) {
   switch (r) {
-    case 1: return pick_sum<1>(nt, plain);
-    case 2: return pick_sum<2>(nt, plain);
-    case 3: return pick_sum<3>(nt, plain);
-    case 4: return pick_sum<4>(nt, plain);
-    case 5: return pick_sum<5>(nt, plain);
-    case 6: return pick_sum<6>(nt, plain);
-    case 7: return pick_sum<7>(nt, plain);
-    case 8: return pick_sum<8>(nt, plain);
+    case 1: return pick_sum<1>(nt, d);
+    case 2: return pick_sum<2>(nt, d);
+    case 3: return pick_sum<3>(nt, d);
+    case 4: return pick_sum<4>(nt, d);
+    case 5: return pick_sum<5>(nt, d);
+    case 6: return pick_sum<6>(nt, d);
+    case 7: return pick_sum<7>(nt, d);
+    case 8: return pick_sum<8>(nt, d);
     default: return nullptr;
   }
 }
@@ -138,7 +147,7 @@ hipError_t launch_zero(float* out, uint64_t count, hipStream_t stream) {
 hipError_t launch_sum(const Plan& plan, const void* x, float* out, void* ws, hipStream_t stream) {
   if (plan.n == 0) return launch_zero(out, 1, stream);
   const void* fn = sum_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
-                                  (plan.flags & ARMX_FLAG_PLAIN) != 0);
+                                  chain_design(plan.flags));
   if (!fn) return hipErrorInvalidValue;
   const u32x4* xv = static_cast<const u32x4*>(x);
   uint64_t n = plan.n;

@@ -410,6 +410,8 @@ def main() -> int:
         ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], plain=True), 200)
         var["plain_shuffle_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6,
                                      "vs_mfma": avg_ms / ms}
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], all_ones=True), 200)
+        var["mfma_all_ones_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "vs_signed": avg_ms / ms}
         ms, med = event_timed(torch, lambda i: armx.reduce_sum(
             bufs[i & 1], one_chain=True, block_threads=256, chain_r=4), 50)
         var["one_chain_b256_r4_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
@@ -469,6 +471,7 @@ def main() -> int:
         xs30 = torch.from_numpy(stress_np).to(dev)
         var["precision_2p30_logu"] = {
             "mfma": float(armx.reduce_sum(xs30).item()),
+            "mfma_all_ones": float(armx.reduce_sum(xs30, all_ones=True).item()),
             "plain": float(armx.reduce_sum(xs30, plain=True).item()),
             "exact_result_bits": int(armx.reduce_sum_exact(xs30).cpu().numpy().view(np.uint32)),
         }
@@ -674,6 +677,7 @@ def main() -> int:
             record["check"]["precision_2p30_logu"] = {
                 "exact_sum": e30.f64, "abs_sum": e30.abs_sum,
                 "rel_err_mfma": abs(p30["mfma"] - e30.f64) / abs(e30.f64),
+                "rel_err_mfma_all_ones": abs(p30["mfma_all_ones"] - e30.f64) / abs(e30.f64),
                 "rel_err_plain": abs(p30["plain"] - e30.f64) / abs(e30.f64),
                 "exact_variant_matches_oracle":
                     p30["exact_result_bits"] == int(np.float32(e30.f32).view(np.uint32)),

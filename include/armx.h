@@ -85,6 +85,10 @@ typedef enum armx_status {
 #define ARMX_FLAG_MMA_LEAVES 0x20u /* the two fixed-order entry points: the    */
                                    /* order whose leaves are MFMAs (see        */
                                    /* reduce_sum_fixed_order)                  */
+#define ARMX_FLAG_ALL_ONES 0x40u   /* reduce_sum / reduce_rows: the MFMA       */
+                                   /* design with the literal all-ones operand */
+                                   /* (see reduce_sum); not with PLAIN or      */
+                                   /* MMA_LEVELS                               */
 
 typedef struct armx_config {
   int block_threads; /* 0 = default; else 64..1024, a multiple of 64.         */
@@ -133,13 +137,23 @@ typedef struct armx_config {
  * n        element count, 0 .. 2^40.
  * out      device, 1 binary32; n == 0 writes +0.0.
  * ws       device workspace (see conventions), ws_bytes its size.
- * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
+ * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design,
+ *          ARMX_FLAG_ALL_ONES the all-ones operand.
  *
- * Each wavefront multiplies an all-ones 16x32 fp16 matrix by 32x16 tiles of
- * x (one 16-byte load per lane) with v_mfma_f32_16x16x32_f16, chaining R of
- * them into fp32 accumulators.  The order of additions depends on the
- * configuration (not on timing): two calls with the same n, configuration
- * and device give the same bits.
+ * Each wavefront multiplies a constant 16x32 fp16 matrix of ones by 32x16
+ * tiles of x (one 16-byte load per lane) with v_mfma_f32_16x16x32_f16,
+ * chaining R of them into fp32 accumulators.  By default the ones matrix has
+ * its lower 8 rows negated: D's upper rows accumulate the 16 column sums and
+ * its lower rows their negations, each element on its own, and the result is
+ * half the difference of the two totals.  The MFMA's accumulation on gfx950
+ * cuts some low bits toward minus infinity, which makes an all-ones sum lean
+ * low on data of wide dynamic range (measured: -10 on a sum of 2^30 values
+ * whose exact value is 9797); the negated sums lean the other way by the
+ * same amount in distribution, so the difference cancels the lean.  It costs
+ * no instruction per load.  ARMX_FLAG_ALL_ONES selects the literal all-ones
+ * operand (every output row a column sum; the total read from one row).  The
+ * order of additions depends on the configuration (not on timing): two calls
+ * with the same n, configuration and device give the same bits.
  *
  * With ARMX_FLAG_MMA_LEVELS the sum is computed in the recursive form whose
  * level count the same Abstract's running-time model T(n) = 5 log_{m^2}(n)
@@ -179,7 +193,8 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
  *          last block to finish combines in a fixed order; with ws NULL
  *          those rows are summed as without a split (slower, and in another
  *          order).  Otherwise ws is not used.
- * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design.
+ * cfg      host, may be NULL.  ARMX_FLAG_PLAIN selects the MFMA-free design,
+ *          ARMX_FLAG_ALL_ONES the all-ones operand (see reduce_sum).
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  *
  * Rows of at most 512 values are summed by lanes (each row on a

@@ -97,13 +97,18 @@ int main(int argc, char** argv) {
       case ARMX_OP_SUM: {
         const unsigned k = unsigned(rng() % 4);
         if (k == 0) return ARMX_FLAG_MMA_LEVELS | unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
-        return unsigned(rng() % 16);   // PLAIN, CACHED_LOADS, ONE_CHAIN, TWO_PASS
+        unsigned f = unsigned(rng() % 16);   // PLAIN, CACHED_LOADS, ONE_CHAIN, TWO_PASS
+        if (!(f & ARMX_FLAG_PLAIN) && rng() % 2) f |= ARMX_FLAG_ALL_ONES;
+        return f;
       }
       case ARMX_OP_FIXED:
         return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
                unsigned(rng() % 2) * ARMX_FLAG_TWO_PASS | unsigned(rng() % 2) * ARMX_FLAG_MMA_LEAVES;
-      case ARMX_OP_ROWS:
-        return unsigned(rng() % 2) * ARMX_FLAG_PLAIN | unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+      case ARMX_OP_ROWS: {
+        const unsigned design = unsigned(rng() % 3);   // signed, plain, all ones
+        return (design == 1 ? ARMX_FLAG_PLAIN : design == 2 ? ARMX_FLAG_ALL_ONES : 0u) |
+               unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+      }
       case ARMX_OP_ROWS_FIXED:
         return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
                unsigned(rng() % 2) * ARMX_FLAG_MMA_LEAVES;
@@ -123,7 +128,7 @@ int main(int argc, char** argv) {
       if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
       c.chain_r = int(rng() % 10);
       c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
-      c.flags = unsigned(rng() % 64);
+      c.flags = unsigned(rng() % 128);
       n = pick_n();
       cols = pick_n() % (uint64_t(1) << 30);
       ld = (rng() % 2) ? cols : cols + (rng() % 64);
@@ -159,6 +164,10 @@ int main(int argc, char** argv) {
            (unsigned long long)R);
     EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || op == ARMX_OP_FIXED || op == ARMX_OP_ROWS_FIXED,
            "MMA leaves accepted for op %d", op);
+    EXPECT(!(p.flags & ARMX_FLAG_ALL_ONES) ||
+               ((op == ARMX_OP_SUM || op == ARMX_OP_ROWS) &&
+                !(p.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_MMA_LEVELS))),
+           "all-ones operand accepted for op %d flags 0x%x", op, p.flags);
     const bool levels = (p.flags & ARMX_FLAG_MMA_LEVELS) != 0;
     EXPECT(!levels || op == ARMX_OP_SUM, "levels flag accepted for op %d", op);
     if (levels) {

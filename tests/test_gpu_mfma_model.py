@@ -3,9 +3,9 @@
 as "Taming Bitwise Behavior in GPU Kernels with Tensor Core" (arXiv
 2609.11356, Abstract) does for closed libraries.
 
-A row of reduce_rows with R x 512 values (then a chain of zeros) whose only
-non-zero values sit in MFMA column 0 returns exactly that column's chain of R
-MFMAs: the other 15 column sums are zero and the combines only add zeros.  Column 0's
+A row of reduce_rows with the all-ones operand (ARMX_FLAG_ALL_ONES) and R x
+512 values (then a chain of zeros) whose only non-zero values sit in MFMA
+column 0 returns exactly that column's chain of R MFMAs: the other 15 column sums are zero and the combines only add zeros.  Column 0's
 K position k is element (k // 8) * 128 + k % 8 of each 512-value tile (lane
 16 (k // 8) holds K values 8 (k // 8) .. + 7 of column 0)."""
 import numpy as np
@@ -38,7 +38,8 @@ def gpu_chains(tiles: np.ndarray) -> np.ndarray:
     x = np.zeros((n, 512 * (R + 1)), np.float16)
     for r in range(R):
         x[:, r * 512 + KPOS] = tiles[:, r, :]
-    return armx.reduce_rows(to_dev(x), chain_r=R, block_threads=64).cpu().numpy()
+    return armx.reduce_rows(to_dev(x), chain_r=R, block_threads=64,
+                            all_ones=True).cpu().numpy()
 
 
 def col(*pairs):

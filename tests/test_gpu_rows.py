@@ -28,8 +28,9 @@ def check_rows(x, got, what=""):
 
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 8), (5, 1000), (17, 513), (64, 4096),
                                        (33, 2048 * 5 + 7), (2, 300_000)])
-@pytest.mark.parametrize("plain", [False, True])
-def test_shapes(rows, cols, plain):
+@pytest.mark.parametrize("design", [dict(), dict(plain=True), dict(all_ones=True)],
+                         ids=["signed", "plain", "ones"])
+def test_shapes(rows, cols, design):
     x = si.generate_rows("normal", rows, cols, seed=rows * 7 + cols)
     if cols % 8:
         # rows must start 16-byte aligned: pad the pitch, sum only `cols`
@@ -39,8 +40,8 @@ def test_shapes(rows, cols, plain):
         xd = to_dev(pad)[:, :cols]
     else:
         xd = to_dev(x)
-    got = armx.reduce_rows(xd, plain=plain).cpu().numpy()
-    check_rows(x, got, f"{rows}x{cols} plain={plain}")
+    got = armx.reduce_rows(xd, **design).cpu().numpy()
+    check_rows(x, got, f"{rows}x{cols} {design}")
 
 
 @pytest.mark.parametrize("block", [64, 256, 1024])
@@ -94,7 +95,7 @@ def test_many_rows_flat_pipeline(rows, cols):
     # rows that are whole numbers of chains take the cross-row pipelined path
     x = si.generate_rows("uniform11", rows, cols, seed=rows)
     xd = to_dev(x)
-    for cfg in (dict(), dict(plain=True), dict(chain_r=4, block_threads=64)):
+    for cfg in (dict(), dict(plain=True), dict(all_ones=True), dict(chain_r=4, block_threads=64)):
         got = armx.reduce_rows(xd, **cfg).cpu().numpy()
         check_rows(x, got, str(cfg))
 

@@ -64,10 +64,12 @@ def test_free_order_split(rows, cols):
     again = armx.reduce_rows(xd).cpu().numpy()
     assert np.array_equal(bits(got), bits(again))           # same bits every call
     plain = armx.reduce_rows(xd, plain=True).cpu().numpy()
+    ones = armx.reduce_rows(xd, all_ones=True).cpu().numpy()
     unsplit = no_workspace(armx.lib.reduce_rows, xd)
     for r, e in enumerate(exact_row_sums(x)):
         check_free_order(float(got[r]), e, f"row {r}")
         check_free_order(float(plain[r]), e, f"plain row {r}")
+        check_free_order(float(ones[r]), e, f"all-ones row {r}")
         check_free_order(float(unsplit[r]), e, f"unsplit row {r}")
 
 
