@@ -35,7 +35,7 @@ import torch
 
 __all__ = [
     "reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
-    "reduce_sum_exact", "fixed_to_int", "workspace_bytes", "launch_plan", "ArmxError", "Config",
+    "reduce_sum_exact", "reduce_sum_noalloc", "fixed_to_int", "workspace_bytes", "launch_plan", "ArmxError", "Config",
     "PlanInfo", "LIB_PATH",
     "OP_SUM", "OP_ROWS", "OP_FIXED", "OP_ROWS_FIXED", "OP_EXACT",
     "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS", "FLAG_MMA_LEVELS",
@@ -94,8 +94,9 @@ def _load() -> ctypes.CDLL:
     lib.reduce_rows.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_rows_fixed_order.argtypes = [vp, sz, sz, sz, vp, vp, sz, cfgp, vp]
     lib.reduce_sum_exact.argtypes = [vp, sz, vp, vp, vp, sz, cfgp, vp]
+    lib.reduce_sum_noalloc.argtypes = [vp, sz, vp, cfgp, vp]
     for f in (lib.reduce_sum, lib.reduce_sum_fixed_order, lib.reduce_rows,
-              lib.reduce_rows_fixed_order, lib.reduce_sum_exact):
+              lib.reduce_rows_fixed_order, lib.reduce_sum_exact, lib.reduce_sum_noalloc):
         f.restype = ctypes.c_int
     lib.armx_workspace_bytes.argtypes = [ctypes.c_int, sz, sz, cfgp]
     lib.armx_workspace_bytes.restype = sz
@@ -254,6 +255,27 @@ def reduce_sum(x: torch.Tensor, *, out: torch.Tensor | None = None,
     passed explicitly must be zero-filled before its first use.
     """
     return _flat_call(lib.reduce_sum, OP_SUM, x, out, workspace, _config(**cfg), "reduce_sum")
+
+
+def reduce_sum_noalloc(x: torch.Tensor, *, out: torch.Tensor, **cfg) -> torch.Tensor:
+    """reduce_sum into a caller-allocated ``out`` (a float32 GPU tensor) with
+    no workspace: the library's static per-device scratch array stands in
+    for it, so the call allocates nothing.  Calls that may overlap on one
+    device race on that array."""
+    _check_input(x, None, "reduce_sum_noalloc")
+    if not x.is_contiguous():
+        raise ValueError("reduce_sum_noalloc: the input must be contiguous")
+    dev = x.device
+    if out.dtype != torch.float32 or out.device != dev or out.numel() < 1:
+        raise ValueError(f"reduce_sum_noalloc: out must be a float32 tensor on {dev}")
+    n = x.numel()
+    with _on_device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        c = _config(**cfg)
+        st = lib.reduce_sum_noalloc(x.data_ptr() if n else None, n, out.data_ptr(),
+                                    ctypes.byref(c), stream)
+    _check(st, "reduce_sum_noalloc")
+    return out
 
 
 def reduce_sum_fixed_order(x: torch.Tensor, *, out: torch.Tensor | None = None,

@@ -127,6 +127,33 @@ int reduce_sum(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
   return hip_status(armx::launch_sum(plan, x, out, ws, static_cast<hipStream_t>(stream)));
 }
 
+int reduce_sum_noalloc(const void* x, size_t n, float* out, const armx_config* cfg,
+                       void* stream) {
+  armx::Plan plan;
+  if (!out) return ARMX_ERR_NULL;
+  if (n > 0 && !x) return ARMX_ERR_NULL;
+  if (n > 0 && !aligned(x, 16)) return ARMX_ERR_ALIGN;
+  int st = armx::make_plan(armx::kOpSum, n, 0, 0, cfg, 256, &plan);
+  if (st != ARMX_OK) return st;
+  st = armx::make_plan(armx::kOpSum, n, 0, 0, cfg, n > 0 ? current_cu_count() : 256, &plan);
+  if (st != ARMX_OK) return st;
+  if (plan.ws_bytes > armx::kScratchBytes) return ARMX_ERR_WORKSPACE;
+  log_plan("reduce_sum_noalloc", plan);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    if (armx::scratch_address(&ws) != hipSuccess) return ARMX_ERR_HIP;
+    // the completion counters must start at zero: cleared by a small kernel
+    // on the caller's stream (capturable; no memset, no allocation)
+    const hipError_t e =
+        armx::launch_zero(static_cast<float*>(ws), armx::kCounterBytes / sizeof(float), s);
+    if (e != hipSuccess) return ARMX_ERR_HIP;
+  }
+  if (plan.flags & ARMX_FLAG_MMA_LEVELS)
+    return hip_status(armx::launch_levels(plan, x, out, ws, s));
+  return hip_status(armx::launch_sum(plan, x, out, ws, s));
+}
+
 int reduce_sum_fixed_order(const void* x, size_t n, float* out, void* ws, size_t ws_bytes,
                            const armx_config* cfg, void* stream) {
   armx::Plan plan;

@@ -80,4 +80,9 @@ hipError_t launch_short_rows(const Plan& plan, const void* x, float* out, hipStr
 // be captured in a graph and replayed).
 hipError_t launch_zero(float* out, uint64_t count, hipStream_t stream);
 
+// Device address, on the current device, of the static scratch array that
+// reduce_sum_noalloc uses as its workspace (kScratchBytes bytes, 256-byte
+// aligned); looked up with hipGetSymbolAddress on the first call per device.
+hipError_t scratch_address(void** ptr);
+
 }  // namespace armx

@@ -52,6 +52,9 @@ constexpr size_t kFixedLdsBytes = 64 * 1024;
 constexpr size_t kCounterBytes = 256;
 constexpr unsigned kMaxGroups = 63;
 constexpr uint64_t kMaxN = uint64_t(1) << 40;
+// The static scratch array of reduce_sum_noalloc (one per device): calls
+// whose plan needs a larger workspace are refused.
+constexpr size_t kScratchBytes = size_t(1) << 20;
 
 enum Op {
   kOpSum = ARMX_OP_SUM,

@@ -30,6 +30,9 @@
 // lets the last block of each group and then the last group reduce the
 // results in index order (or a second launch does, with ARMX_FLAG_TWO_PASS).
 // No data atomics are used, so the result depends only on the configuration.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.h"
 
@@ -134,7 +137,40 @@ const void* sum_kernel_for(int r, bool nt, int d) {
   }
 }
 
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch[kScratchDevices];
+std::mutex g_scratch_mutex;
+
 }  // namespace
+
+// Scratch memory of the allocation-free entry point (reduce_sum_noalloc): the
+// counter region and block results that reduce_sum keeps in the caller's
+// workspace, here in one static device array per GPU, held until the process
+// ends.  Host code never passes `scratch` itself (in host code that name is a
+// stand-in, not a device address): scratch_address() looks its device
+// address up once per device with hipGetSymbolAddress and every use goes
+// through that pointer.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_zero(float* out, uint64_t count, hipStream_t stream) {
   if (count == 0) return hipSuccess;

@@ -318,6 +318,32 @@ int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, 
 int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, void* ws,
                      size_t ws_bytes, const armx_config* cfg, void* stream);
 
+/*
+ * reduce_sum_noalloc -- reduce_sum without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same result, arguments and configuration as reduce_sum (the same bits as
+ * reduce_sum with the same n, configuration and device), but the counter
+ * region and block results live in a static device array of the library, 1
+ * MiB per GPU, reserved when the library is loaded and held until the
+ * process ends.  Each call first clears the array's 256-byte counter region
+ * with a small kernel on `stream`, then launches reduce_sum's kernels on it;
+ * it calls no hipMalloc, hipFree or other allocating routine.  On its first
+ * call on a device it looks up the array's device address
+ * (hipGetSymbolAddress) with that device current.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one device (different streams, or graphs replayed concurrently) race and
+ * must be serialised by the caller.
+ * Returns ARMX_OK, ARMX_ERR_{NULL,ALIGN,CONFIG,SHAPE,HIP} as reduce_sum, or
+ * ARMX_ERR_WORKSPACE when the configuration needs more than 1 MiB of
+ * workspace (armx_workspace_bytes(ARMX_OP_SUM, ...) > 1048576: e.g. the
+ * one-chain grid of ARMX_FLAG_ONE_CHAIN with small blocks and R on large
+ * inputs, or ARMX_FLAG_MMA_LEVELS beyond about 2^30 values at R = 8).
+ */
+int reduce_sum_noalloc(const void* x, size_t n, float* out, const armx_config* cfg,
+                       void* stream);
+
 /* Operation codes for armx_workspace_bytes. */
 #define ARMX_OP_SUM 0
 #define ARMX_OP_ROWS 1

@@ -26,7 +26,7 @@ def test_header_declares_the_three_entry_points():
     names = _declared_functions()
     for f in ("reduce_sum", "reduce_rows", "reduce_sum_fixed_order", "reduce_rows_fixed_order",
               "reduce_sum_exact", "armx_workspace_bytes", "armx_status_string", "armx_version",
-              "armx_launch_plan"):
+              "armx_launch_plan", "reduce_sum_noalloc"):
         assert f in names
 
 
@@ -67,6 +67,21 @@ def test_launch_plan_reports_the_planned_shape():
     with pytest.raises(armx.ArmxError):
         armx.launch_plan(armx.OP_SUM, 10, block_threads=96)
     assert armx.lib.armx_launch_plan(0, 10, 0, None, None) == -1
+
+
+def test_noalloc_argument_errors():
+    f = armx.lib.reduce_sum_noalloc
+    assert f(None, 10, FAKE, None, None) == -1                           # x NULL
+    assert f(FAKE, 10, None, None, None) == -1                           # out NULL
+    assert f(FAKE + 2, 10, FAKE, None, None) == -2                       # x misaligned
+    assert f(FAKE, 10, FAKE, cfg(block_threads=96), None) == -3
+    # a plan whose workspace exceeds the 1 MiB scratch array is refused
+    # before anything is enqueued: the one-chain grid of 64-thread blocks at
+    # R = 1 has 2^28 / 512 blocks, 4 bytes of block result each
+    assert f(FAKE, 1 << 28, FAKE, cfg(one_chain=True, block_threads=64, chain_r=1), None) == -4
+    assert armx.workspace_bytes(armx.OP_SUM, 1 << 28, one_chain=True, block_threads=64,
+                                chain_r=1) > 1 << 20
+    assert armx.workspace_bytes(armx.OP_SUM, 1 << 40) <= 1 << 20   # every default plan fits
 
 
 def cfg(**kw):
