@@ -9,9 +9,11 @@ previous step left in the 256 MB Infinity Cache.
 Prints ONE JSON line.  `value` is elements/s over the timed steps (wall clock
 between two synchronisations; each step one call through the C ABI, nothing
 else in the loop); `roofline.achieved` is the algorithmic bytes of one launch
-(2 bytes per element) divided by the average kernel time, measured with HIP
-events that the kernel's own dispatch stamps (hipExtLaunchKernel) on the
-stream it runs on, in a pass of its own after the timed steps.  `cpu_baseline`
+(2 bytes per element) divided by the average kernel time: the elapsed time of
+HIP events recorded on the kernel's stream around the timed steps (the
+kernels run back to back), over the step count.  As a cross-check, a pass of
+its own after the timed steps times single launches with HIP events that the
+kernel's own dispatch stamps (hipExtLaunchKernel).  `cpu_baseline`
 is the CPU oracle timed on this host: the exact integer sum and the
 balanced-tree emulator, each on one thread and on all the host threads it may
 use; its results also give `check`, the errors of the headline, of every
@@ -323,14 +325,22 @@ def main() -> int:
         if st != 0:
             raise RuntimeError(f"reduce_sum returned {st}")
 
+    # HIP events on the stream the kernel runs on bracket the timed region:
+    # the kernels run back to back, so their elapsed time over the step count
+    # is the average launch duration (each launch's own time plus the few
+    # nanoseconds between dispatches).
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record()
     for i in range(args.steps):
         step(i)
+    region[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    region_ms = region[0].elapsed_time(region[1])
     result = float(out.item())
 
     # Per-launch timing, in a pass of its own after the timed steps: HIP
@@ -349,7 +359,8 @@ def main() -> int:
         armx.reduce_sum(bufs[i & 1], out=out, workspace=ws, start_event=ev[0], stop_event=ev[1])
     torch.cuda.synchronize()
     launch_ms = sorted(s_ev.elapsed_time(e_ev) for s_ev, e_ev in evs.values())
-    avg_ms = sum(launch_ms) / len(launch_ms)
+    stamped_avg_ms = sum(launch_ms) / len(launch_ms)
+    avg_ms = region_ms / args.steps
 
     bytes_per_launch = 2 * n
     achieved = bytes_per_launch / (avg_ms * 1e-3) / 1e9
@@ -383,10 +394,15 @@ def main() -> int:
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
             "kernel": f"sum_kernel<R={head_plan['chain_r']}, non-temporal, MFMA>",
-            "launch_ms_avg": avg_ms, "launch_ms_median": launch_ms[len(launch_ms) // 2],
-            "launch_ms_p10": launch_ms[len(launch_ms) // 10],
-            "launch_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
-            "launches_timed": len(launch_ms),
+            "launch_ms_avg": avg_ms,
+            "launch_timing": "HIP events on the kernel's stream around the timed steps, "
+                             "elapsed time / steps",
+            "launches_timed": args.steps,
+            "stamped_launch_ms_avg": stamped_avg_ms,
+            "stamped_launch_ms_median": launch_ms[len(launch_ms) // 2],
+            "stamped_launch_ms_p10": launch_ms[len(launch_ms) // 10],
+            "stamped_launch_ms_p90": launch_ms[(9 * len(launch_ms)) // 10],
+            "stamped_launches": len(launch_ms),
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "kernel_source_sha256_16": kernel_source_hash(),
         },
