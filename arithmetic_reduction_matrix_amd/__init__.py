@@ -39,7 +39,7 @@ __all__ = [
     "PlanInfo", "LIB_PATH",
     "OP_SUM", "OP_ROWS", "OP_FIXED", "OP_ROWS_FIXED", "OP_EXACT",
     "FLAG_PLAIN", "FLAG_CACHED_LOADS", "FLAG_ONE_CHAIN", "FLAG_TWO_PASS", "FLAG_MMA_LEVELS",
-    "FLAG_MMA_LEAVES", "FLAG_ALL_ONES",
+    "FLAG_MMA_LEAVES", "FLAG_ALL_ONES", "FLAG_INT_LIMBS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libarmx.so")
@@ -49,6 +49,7 @@ FLAG_PLAIN, FLAG_CACHED_LOADS, FLAG_ONE_CHAIN, FLAG_TWO_PASS = 0x1, 0x2, 0x4, 0x
 FLAG_MMA_LEVELS = 0x10
 FLAG_MMA_LEAVES = 0x20
 FLAG_ALL_ONES = 0x40
+FLAG_INT_LIMBS = 0x80
 
 _STATUS = {
     0: "ARMX_OK", -1: "ARMX_ERR_NULL", -2: "ARMX_ERR_ALIGN", -3: "ARMX_ERR_CONFIG",
@@ -123,11 +124,11 @@ def _event_handle(ev) -> int | None:
 
 def _config(block_threads=0, chain_r=0, grid_blocks=0, plain=False, cached_loads=False,
             one_chain=False, two_pass=False, mma_levels=False, mma_leaves=False,
-            all_ones=False, start_event=None, stop_event=None) -> Config:
+            all_ones=False, int_limbs=False, start_event=None, stop_event=None) -> Config:
     flags = ((FLAG_PLAIN if plain else 0) | (FLAG_CACHED_LOADS if cached_loads else 0)
              | (FLAG_ONE_CHAIN if one_chain else 0) | (FLAG_TWO_PASS if two_pass else 0)
              | (FLAG_MMA_LEVELS if mma_levels else 0) | (FLAG_MMA_LEAVES if mma_leaves else 0)
-             | (FLAG_ALL_ONES if all_ones else 0))
+             | (FLAG_ALL_ONES if all_ones else 0) | (FLAG_INT_LIMBS if int_limbs else 0))
     return Config(int(block_threads), int(chain_r), int(grid_blocks), flags,
                   _event_handle(start_event), _event_handle(stop_event))
 

@@ -21,9 +21,16 @@
 //  * wavefront, block and grid combines add these integers, folding the low
 //    limb's carries into the high one so every term stays below 2^32; the
 //    last block (completion ticket) rounds the 128-bit total once.
-// No MFMA: the operation is bound by HBM bandwidth, and feeding an integer
-// MFMA would first need every value split into 8-bit limbs, which costs more
-// vector instructions per value than the binary64 additions do.
+// That default form uses no MFMA.  ARMX_FLAG_INT_LIMBS selects the form
+// whose sums are integer MFMAs over 8-bit limbs (the limb planes of the AWE
+// Abstract): every value's count q (|q| < 2^40) is written as eight signed
+// 8-bit digits d_0 .. d_7 with q = s + sum_m d_m 2^(8m) (s = 1 for a negative
+// value, else 0; see value_digits), and v_mfma_i32_16x16x64_i8 against a
+// digit-selector operand adds, per output column, the digits of each
+// position m over 8 values per MFMA -- exact in 32-bit integers -- so the
+// digit planes are summed by the matrix cores and recombined with their
+// weights 2^(8m) at the end.  Building the digits costs about a dozen
+// vector instructions per value, against three for the binary64 form.
 //
 // Non-finite inputs: a chain whose binary64 sum is not finite sets a flag
 // (+Inf, -Inf or NaN) instead of adding to the integers; the result follows
@@ -73,14 +80,138 @@ __device__ __forceinline__ void add_chain(const u32x4 (&v)[R], Exact& a) {
   a.lo += uint64_t(unsigned(l));
 }
 
+// ---- the integer-MFMA limb form ------------------------------------------
+//
+// Digits of one value.  A finite binary16 value is q 2^-24 with q = +-M 2^t,
+// M = the significand with its hidden bit (f, or 1024 + f), t = e - 1 (0 for
+// subnormals, e the exponent field), |q| < 2^40.  Let g = |q| xor (all ones
+// if negative), so g = q for q >= 0 and g = q - 1 for q < 0 (two's
+// complement), and y = g + C with C = 0x8080808080808080.  The bytes y_m of y
+// read as signed 8-bit digits after flipping their top bit, d_m = y_m - 128
+// (y_m xor 0x80 as int8), satisfy sum_m d_m 2^(8m) = y - C; and g + C lies in
+// [0, 2^64) because |g| < 2^40, so y = g + C with no wrap-around and the
+// digits give g exactly: q = s + sum_m d_m 2^(8m) with s = 1 for a negative
+// value.  The eight digits are returned as
+// the bytes of one 64-bit word (digit m in byte m).  An exponent field of 31
+// (infinity, NaN) gives digits of no meaning; such chains are flagged apart.
+__device__ __forceinline__ uint64_t value_digits(uint32_t h) {
+  constexpr uint64_t C = 0x8080808080808080ull;
+  const uint32_t e = (h >> 10) & 31u;
+  const uint32_t mn = __builtin_elementwise_min(e, 1u);
+  const uint32_t m = (mn << 10) | (h & 1023u);
+  const uint64_t mag = uint64_t(m) << (e - mn);
+  const uint32_t s32 = uint32_t(int32_t(h << 16) >> 31);   // 0 or all ones
+  const uint64_t g = mag ^ (uint64_t(s32) << 32 | s32);
+  return (g + C) ^ C;
+}
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+
+// The digit selector: A of v_mfma_i32_16x16x64_i8 with A[i][k] = 1 when
+// k mod 8 == i < 8, else 0.  Lane l supplies row l % 16 over 16 K positions
+// (two 8-aligned runs of K, byte b at a K index congruent to b mod 8), so
+// its bytes b and b + 8 with b == l % 16 are 1 for l % 16 < 8; rows 8-15 are
+// zero.  Output row i (< 8) of column j then adds digit i of the 8 values
+// whose digits fill column j of B.
+__device__ __forceinline__ int4v digit_selector(int lane) {
+  const int i = lane & 15;
+  int4v a = {0, 0, 0, 0};
+  if (i < 8) {
+    const int one = 1 << (8 * (i & 3));
+    a[i >> 2] = one;
+    a[(i >> 2) + 2] = one;
+  }
+  return a;
+}
+
+// Per-lane state of the limb form: the digit-position sums of this lane's
+// accumulator rows (lane l holds rows 4 (l / 16) .. + 3 of column l % 16:
+// digit positions 0-3 in lanes 0-15, 4-7 in lanes 16-31, zero in lanes
+// 32-63), the count of negative values this lane loaded (the s terms), and
+// the largest exponent field it loaded (31: an infinity or a NaN).
+struct LimbSums {
+  int64_t pos[4];
+  uint64_t negatives;
+  uint32_t expo;   // the largest exponent field (bits 10-14) of any value seen
+};
+
+// One chain of R loads (8 R values per lane): 4 R integer MFMAs (two values'
+// digits, 16 bytes, per lane each) into two accumulators in turn (so that
+// consecutive MFMAs do not wait for each other), exact in 32 bits within the
+// chain (8 digits of at most 128 in magnitude per element per MFMA), then
+// added into the 64-bit sums.  Values with exponent field 31 (infinity,
+// NaN) give digits of no meaning; the largest exponent field is kept, and a
+// wavefront that saw 31 works out the non-finite flags after its stream.
+template <int R>
+__device__ __forceinline__ void add_chain_limbs(const u32x4 (&v)[R], const int4v sel,
+                                                LimbSums& ls) {
+  int4v acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  uint32_t expo = ls.expo;
+  unsigned neg = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int w = 0; w < 4; w += 2) {
+      const uint64_t d0 = value_digits(v[r][w] & 0xFFFFu);
+      const uint64_t d1 = value_digits(v[r][w] >> 16);
+      const uint64_t d2 = value_digits(v[r][w + 1] & 0xFFFFu);
+      const uint64_t d3 = value_digits(v[r][w + 1] >> 16);
+      const int4v b01 = {int(uint32_t(d0)), int(uint32_t(d0 >> 32)), int(uint32_t(d1)),
+                         int(uint32_t(d1 >> 32))};
+      const int4v b23 = {int(uint32_t(d2)), int(uint32_t(d2 >> 32)), int(uint32_t(d3)),
+                         int(uint32_t(d3 >> 32))};
+      acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sel, b01, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sel, b23, acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      neg += __builtin_popcount(v[r][w] & 0x80008000u);
+      const uint32_t ex = v[r][w] & 0x7C007C00u;
+      const uint32_t lo = ex & 0xFFFFu, hi = ex >> 16;
+      expo = expo > lo ? expo : lo;
+      expo = expo > hi ? expo : hi;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) ls.pos[r] += int64_t(acc0[r]) + int64_t(acc1[r]);
+  ls.negatives += neg;
+  ls.expo = expo;
+}
+
+// The lane's limb sums as an Exact (digit position m weighs 2^(8m)).
+__device__ __forceinline__ void limbs_to_exact(const LimbSums& ls, int lane, Exact& a) {
+  const int base = ((lane >> 4) & 1) * 4;   // lanes 32-63 hold zeros
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = base + r;
+    const int64_t v = ls.pos[r];
+    if (m < 4) {
+      const int64_t t = int64_t(uint64_t(v) << (8 * m));
+      a.hi += t >> 32;
+      a.lo += uint64_t(t) & 0xFFFFFFFFull;
+    } else {
+      a.hi += int64_t(uint64_t(v) << (8 * m - 32));
+    }
+  }
+  a.lo += ls.negatives;
+}
+
 // The full chains c0, c0 + stride, ... (`iters` of them), with the load
 // pipeline of the free-order kernel: the next chain's loads are issued before
 // the current chain's additions, ping-pong buffers, clamped prefetch.
-template <int R, bool NT>
+template <int R, bool NT, bool LIMBS>
 __device__ __forceinline__ void stream_exact(const u32x4* __restrict__ x, uint64_t c0,
                                              uint64_t iters, uint64_t stride, int lane,
-                                             Exact& a) {
+                                             Exact& a, LimbSums& ls) {
   if (iters == 0) return;
+  const int4v sel = digit_selector(lane);
+  auto add = [&](const u32x4 (&v)[R]) {
+    if constexpr (LIMBS) {
+      add_chain_limbs<R>(v, sel, ls);
+    } else {
+      add_chain<R>(v, a);
+    }
+  };
   const uint64_t last = c0 + (iters - 1) * stride;
   u32x4 p[R], q[R];
   load_chain<R, NT>(x, c0, lane, p);
@@ -89,12 +220,12 @@ __device__ __forceinline__ void stream_exact(const u32x4* __restrict__ x, uint64
     const uint64_t j = 2 * k;
     load_chain<R, NT>(x, c0 + (j + 1) * stride, lane, q);
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the additions
-    add_chain<R>(p, a);
+    add(p);
     load_chain<R, NT>(x, j + 2 < iters ? c0 + (j + 2) * stride : last, lane, p);
     __builtin_amdgcn_sched_barrier(0);
-    add_chain<R>(q, a);
+    add(q);
   }
-  if (iters & 1) add_chain<R>(p, a);  // p holds the last chain
+  if (iters & 1) add(p);  // p holds the last chain
 }
 
 // Sum over the 64 lanes (every lane gets it); any order, the sums are exact.
@@ -206,8 +337,12 @@ __device__ void finish_exact(Exact a, float* out, int64_t* out_fixed) {
   }
 }
 
-template <int R, bool NT>
-__global__ __launch_bounds__(1024) void exact_kernel(const u32x4* __restrict__ x, uint64_t n,
+// The limb form needs more than the 128 registers per lane a 1024-thread
+// block leaves (its chain holds 16 R digit words besides the loads), so its
+// blocks are bounded to kExactLimbsMaxBlock threads (the plan lowers larger
+// requests; the result never depends on the block size).
+template <int R, bool NT, bool LIMBS>
+__global__ __launch_bounds__(LIMBS ? kExactLimbsMaxBlock : 1024) void exact_kernel(const u32x4* __restrict__ x, uint64_t n,
                                                      uint64_t chains_full,
                                                      unsigned* __restrict__ counters,
                                                      uint64_t* __restrict__ partials,
@@ -222,19 +357,47 @@ __global__ __launch_bounds__(1024) void exact_kernel(const u32x4* __restrict__ x
   uint64_t c = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
 
   Exact a{0, 0, 0};
+  LimbSums ls{{0, 0, 0, 0}, 0, 0};
+  const uint64_t c0 = c;
   const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
-  stream_exact<R, NT>(x, c, iters, total_waves, lane, a);
+  stream_exact<R, NT, LIMBS>(x, c, iters, total_waves, lane, a, ls);
   c += iters * total_waves;
-  if (c == chains_full && chains_full * R * kChunk < n) {
-    // the partial chain at the end: values past n read as +0.0
+  // the partial chain at the end: values past n read as +0.0
+  const bool tail = c == chains_full && chains_full * R * kChunk < n;
+  auto load_tail = [&](u32x4 (&v)[R]) {
     const uint16_t* xh = reinterpret_cast<const uint16_t*>(x);
-    u32x4 v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint64_t e = (c * R + r) * kChunk + uint64_t(lane) * 8;
       v[r] = e < n ? load8_masked(xh, e, n, 0u) : u32x4{0u, 0u, 0u, 0u};
     }
-    add_chain<R>(v, a);
+  };
+  if (tail) {
+    u32x4 v[R];
+    load_tail(v);
+    if constexpr (LIMBS) {
+      add_chain_limbs<R>(v, digit_selector(lane), ls);
+    } else {
+      add_chain<R>(v, a);
+    }
+  }
+  if constexpr (LIMBS) {
+    limbs_to_exact(ls, lane, a);
+    // A wavefront that loaded an infinity or a NaN reads its chains again in
+    // binary64 (add_chain) for the non-finite flags only: a set flag decides
+    // the result and the integers are then not used.  Never taken on finite
+    // data, so the stream above carries no such work.
+    if (__builtin_amdgcn_ballot_w64(ls.expo == 0x7C00u) != 0) {
+      Exact f{0, 0, 0};
+      LimbSums unused{{0, 0, 0, 0}, 0, 0};
+      stream_exact<R, NT, false>(x, c0, iters, total_waves, lane, f, unused);
+      if (tail) {
+        u32x4 v[R];
+        load_tail(v);
+        add_chain<R>(v, f);
+      }
+      a.flags |= f.flags;
+    }
   }
   fold(a);
   const Exact block_total = block_exact(wave_exact(a), lds);
@@ -274,22 +437,27 @@ __global__ void exact_zero_kernel(float* out, int64_t* out_fixed) {
   }
 }
 
-template <int R>
-const void* pick_exact(bool nt) {
-  return nt ? reinterpret_cast<const void*>(&exact_kernel<R, true>)
-            : reinterpret_cast<const void*>(&exact_kernel<R, false>);
+template <int R, bool LIMBS>
+const void* pick_exact_nt(bool nt) {
+  return nt ? reinterpret_cast<const void*>(&exact_kernel<R, true, LIMBS>)
+            : reinterpret_cast<const void*>(&exact_kernel<R, false, LIMBS>);
 }
 
-const void* exact_kernel_for(int r, bool nt) {
+template <int R>
+const void* pick_exact(bool nt, bool limbs) {
+  return limbs ? pick_exact_nt<R, true>(nt) : pick_exact_nt<R, false>(nt);
+}
+
+const void* exact_kernel_for(int r, bool nt, bool limbs) {
   switch (r) {
-    case 1: return pick_exact<1>(nt);
-    case 2: return pick_exact<2>(nt);
-    case 3: return pick_exact<3>(nt);
-    case 4: return pick_exact<4>(nt);
-    case 5: return pick_exact<5>(nt);
-    case 6: return pick_exact<6>(nt);
-    case 7: return pick_exact<7>(nt);
-    case 8: return pick_exact<8>(nt);
+    case 1: return pick_exact<1>(nt, limbs);
+    case 2: return pick_exact<2>(nt, limbs);
+    case 3: return pick_exact<3>(nt, limbs);
+    case 4: return pick_exact<4>(nt, limbs);
+    case 5: return pick_exact<5>(nt, limbs);
+    case 6: return pick_exact<6>(nt, limbs);
+    case 7: return pick_exact<7>(nt, limbs);
+    case 8: return pick_exact<8>(nt, limbs);
     default: return nullptr;
   }
 }
@@ -303,7 +471,8 @@ hipError_t launch_exact(const Plan& plan, const void* x, float* out, int64_t* ou
     return hipLaunchKernel(reinterpret_cast<const void*>(&exact_zero_kernel), dim3(1), dim3(64),
                            args, 0, stream);
   }
-  const void* fn = exact_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0);
+  const void* fn = exact_kernel_for(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
+                                    (plan.flags & ARMX_FLAG_INT_LIMBS) != 0);
   if (!fn) return hipErrorInvalidValue;
   const u32x4* xv = static_cast<const u32x4*>(x);
   uint64_t n = plan.n;

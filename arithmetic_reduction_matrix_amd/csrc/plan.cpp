@@ -10,7 +10,7 @@ namespace {
 constexpr unsigned kKnownFlags = ARMX_FLAG_PLAIN | ARMX_FLAG_CACHED_LOADS |
                                  ARMX_FLAG_ONE_CHAIN | ARMX_FLAG_TWO_PASS |
                                  ARMX_FLAG_MMA_LEVELS | ARMX_FLAG_MMA_LEAVES |
-                                 ARMX_FLAG_ALL_ONES;
+                                 ARMX_FLAG_ALL_ONES | ARMX_FLAG_INT_LIMBS;
 
 uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
 
@@ -176,6 +176,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   const OpDefaults d = op == kOpFixed                    ? kFixedDefaults
                        : op == kOpRows                   ? kRowsDefaults
                        : op == kOpRowsFixed              ? kRowsFixedDefaults
+                       : op == kOpExact && (c.flags & ARMX_FLAG_INT_LIMBS) ? kExactLimbsDefaults
                        : op == kOpExact                  ? kExactDefaults
                        : (c.flags & ARMX_FLAG_MMA_LEVELS) ? kLevelsDefaults
                                                          : kSumDefaults;
@@ -201,14 +202,19 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
   if (op != kOpSum && (c.flags & ARMX_FLAG_MMA_LEVELS)) return ARMX_ERR_CONFIG;
   if (op != kOpFixed && op != kOpRowsFixed && (c.flags & ARMX_FLAG_MMA_LEAVES))
     return ARMX_ERR_CONFIG;
+  if (op != kOpExact && (c.flags & ARMX_FLAG_INT_LIMBS)) return ARMX_ERR_CONFIG;
   // the all-ones operand is a choice of the free-order MFMA design only
   if ((c.flags & ARMX_FLAG_ALL_ONES) &&
       ((op != kOpSum && op != kOpRows) ||
        (c.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_MMA_LEVELS))))
     return ARMX_ERR_CONFIG;
   if (op == kOpExact) {
-    // persistent grid as for the free-order sum; only the load kind is a flag
-    if (c.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS)) return ARMX_ERR_CONFIG;
+    // persistent grid as for the free-order sum; the load kind and the
+    // integer-limb form are the only flags
+    if (c.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS | ARMX_FLAG_INT_LIMBS)) return ARMX_ERR_CONFIG;
+    if ((c.flags & ARMX_FLAG_INT_LIMBS) && p.waves > kExactLimbsMaxBlock / 64)
+      p.waves = kExactLimbsMaxBlock / 64;
+    const uint64_t W = uint64_t(p.waves);
     const uint64_t n = n_or_rows;
     if (n > kMaxN) return ARMX_ERR_SHAPE;
     p.n = n;

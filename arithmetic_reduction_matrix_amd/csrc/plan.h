@@ -41,6 +41,15 @@ constexpr OpDefaults kLevelsDefaults{256, 8, 64};
 constexpr OpDefaults kExactDefaults{128, 8, 16};
 // Exact sum: each block publishes a 32-byte record (two 64-bit limbs, flags).
 constexpr size_t kExactRecordBytes = 32;
+// Largest block of the exact sum's integer-limb form (ARMX_FLAG_INT_LIMBS):
+// its digit words need more registers than a 1024-thread block leaves a lane;
+// a larger requested block is lowered to this.
+constexpr int kExactLimbsMaxBlock = 512;
+// Its defaults: about 16 vector instructions per value make it bound by the
+// vector ALUs, which want every SIMD busy -- measured on MI355X at 2^28 values
+// (us): blocks of 512 at R = 8 (8 wavefronts per CU) 125.5, R = 4 127.3,
+// R = 2 135.1; blocks of 128 at R = 8 (2 per CU) 251.9.
+constexpr OpDefaults kExactLimbsDefaults{512, 8, 16};
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;
 // Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.

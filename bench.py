@@ -437,6 +437,15 @@ def main() -> int:
         exact_val = armx.reduce_sum_exact(bufs[0]).cpu().numpy()
         var["exact_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "vs_free_order": avg_ms / ms,
                              "result_bits": int(exact_val.view(np.uint32))}
+        # the exact sum with integer MFMAs over 8-bit limbs (ARMX_FLAG_INT_LIMBS)
+        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1], int_limbs=True),
+                              200)
+        k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: armx.reduce_sum_exact(
+            bufs[i & 1], int_limbs=True, start_event=s_ev, stop_event=e_ev))
+        limb_val = armx.reduce_sum_exact(bufs[0], int_limbs=True).cpu().numpy()
+        var["exact_int_limbs_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "kernel_ms": k_ms,
+                                       "vs_binary64_form": var["exact_2p28"]["ms"] / ms,
+                                       "result_bits": int(limb_val.view(np.uint32))}
         for r in (8, 4):
             ms, med = event_timed(torch, lambda i: armx.reduce_sum(
                 bufs[i & 1], mma_levels=True, chain_r=r), 200)
@@ -679,6 +688,8 @@ def main() -> int:
             v = record["variants"]
             want = int(np.float32(e.f32).view(np.uint32))
             record["check"]["exact_variant_matches_oracle"] = v["exact_2p28"]["result_bits"] == want
+            record["check"]["exact_int_limbs_matches_oracle"] = (
+                v["exact_int_limbs_2p28"]["result_bits"] == want)
             # every point of the block x R matrix against the exact sum
             # (the 1e-5 relative gate), and fixed order against the emulator
             errs = {k: abs(p["result"] - e.f64) / abs(e.f64)

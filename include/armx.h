@@ -85,6 +85,9 @@ typedef enum armx_status {
 #define ARMX_FLAG_MMA_LEAVES 0x20u /* the two fixed-order entry points: the    */
                                    /* order whose leaves are MFMAs (see        */
                                    /* reduce_sum_fixed_order)                  */
+#define ARMX_FLAG_INT_LIMBS 0x80u  /* reduce_sum_exact: the sums as integer    */
+                                   /* MFMAs over 8-bit limbs (see              */
+                                   /* reduce_sum_exact)                        */
 #define ARMX_FLAG_ALL_ONES 0x40u   /* reduce_sum / reduce_rows: the MFMA       */
                                    /* design with the literal all-ones operand */
                                    /* (see reduce_sum); not with PLAIN or      */
@@ -106,7 +109,8 @@ typedef struct armx_config {
 /* Defaults (block_threads, chain_r), measured on MI355X:
  *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8;
  *   reduce_rows_fixed_order 64, 4; reduce_sum with ARMX_FLAG_MMA_LEVELS
- *   256, 8; reduce_sum_exact 128, 8.
+ *   256, 8; reduce_sum_exact 128, 8 (with ARMX_FLAG_INT_LIMBS 512, 8, and
+ *   larger blocks lowered to 512).
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
  * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth;
  * 64 / R for the MMA-levels form), and at least one block per compute
@@ -309,10 +313,19 @@ int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, 
  *            as a 128-bit two's complement count of 2^-24 (out_fixed[0] the
  *            low 64 bits, out_fixed[1] the high 64 bits, signed); 0 when an
  *            input is an infinity or a NaN.
- * cfg        host, may be NULL.  Only ARMX_FLAG_CACHED_LOADS is accepted.
- * Each lane adds a chain's 8 R values in binary64 (exact: every partial sum
- * is a multiple of 2^-24 below 2^22), and the chain totals accumulate as
- * integers; no MFMA is used.
+ * cfg        host, may be NULL.  Only ARMX_FLAG_CACHED_LOADS and
+ *            ARMX_FLAG_INT_LIMBS are accepted.
+ * By default each lane adds a chain's 8 R values in binary64 (exact: every
+ * partial sum is a multiple of 2^-24 below 2^22), and the chain totals
+ * accumulate as integers; no MFMA is used.  With ARMX_FLAG_INT_LIMBS every
+ * value's count of 2^-24 is written as eight signed 8-bit digits (its limbs,
+ * weights 2^(8m)), and v_mfma_i32_16x16x64_i8 against a digit-selector
+ * operand sums each digit position exactly in 32-bit integers -- the integer
+ * matrix cores do the additions -- before the positions are recombined with
+ * their weights; same result bits, but about 16 vector instructions per
+ * value to form the digits against 3 for the binary64 form, so it is bound
+ * by the vector ALUs (measured on MI355X at 2^28 values: 125 us against
+ * 77 us); the binary64 form is the default for that reason.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  */
 int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, void* ws,

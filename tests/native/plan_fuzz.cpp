@@ -112,8 +112,9 @@ int main(int argc, char** argv) {
       case ARMX_OP_ROWS_FIXED:
         return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
                unsigned(rng() % 2) * ARMX_FLAG_MMA_LEAVES;
-      default:
-        return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS;
+      default:   // exact sum
+        return unsigned(rng() % 2) * ARMX_FLAG_CACHED_LOADS |
+               unsigned(rng() % 2) * ARMX_FLAG_INT_LIMBS;
     }
   };
   int accepted = 0;
@@ -128,7 +129,7 @@ int main(int argc, char** argv) {
       if (rng() % 2) c.block_threads = 64 * int(1 + rng() % 16);
       c.chain_r = int(rng() % 10);
       c.grid_blocks = (rng() % 3 == 0) ? int(rng() % 5000) - 5 : 0;
-      c.flags = unsigned(rng() % 128);
+      c.flags = unsigned(rng() % 256);
       n = pick_n();
       cols = pick_n() % (uint64_t(1) << 30);
       ld = (rng() % 2) ? cols : cols + (rng() % 64);
@@ -164,6 +165,8 @@ int main(int argc, char** argv) {
            (unsigned long long)R);
     EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || op == ARMX_OP_FIXED || op == ARMX_OP_ROWS_FIXED,
            "MMA leaves accepted for op %d", op);
+    EXPECT(!(p.flags & ARMX_FLAG_INT_LIMBS) || op == ARMX_OP_EXACT,
+           "integer limbs accepted for op %d", op);
     EXPECT(!(p.flags & ARMX_FLAG_ALL_ONES) ||
                ((op == ARMX_OP_SUM || op == ARMX_OP_ROWS) &&
                 !(p.flags & (ARMX_FLAG_PLAIN | ARMX_FLAG_MMA_LEVELS))),
@@ -190,7 +193,9 @@ int main(int argc, char** argv) {
       continue;
     }
     if (op == ARMX_OP_EXACT) {
-      EXPECT(!(p.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS)), "exact flags");
+      EXPECT(!(p.flags & ~unsigned(ARMX_FLAG_CACHED_LOADS | ARMX_FLAG_INT_LIMBS)), "exact flags");
+      EXPECT(!(p.flags & ARMX_FLAG_INT_LIMBS) || W * 64 <= armx::kExactLimbsMaxBlock,
+             "limb form block %llu", (unsigned long long)(W * 64));
       if (p.n == 0) continue;
       EXPECT(p.grid >= 1 && uint64_t(p.grid) <= cdiv(cdiv(p.n, 512 * R), W), "exact grid");
       EXPECT(pow2(p.group) && cdiv(uint64_t(p.grid), p.group) <= armx::kMaxGroups, "groups");

@@ -5,7 +5,9 @@ The operation is the arithmetic reduction of "GPU Tensor Cores for fast
 Arithmetic Reductions" (arXiv 2001.05585, Abstract) kept free of rounding
 error up to the final 32-bit result; the sum is carried as integer limbs with
 fixed weights, the representation of "AWE: Adaptive Weight Encoding ..."
-(arXiv 2609.24519, Abstract)."""
+(arXiv 2609.24519, Abstract).  Both forms are checked: binary64 chain sums
+into two 32-bit limbs (the default), and eight signed 8-bit limbs per value
+summed by integer MFMAs (ARMX_FLAG_INT_LIMBS)."""
 import math
 
 import numpy as np
@@ -19,6 +21,10 @@ from oracle import exact_sum
 from _parity import bits32, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
+
+
+FORMS = {"binary64": {}, "int_limbs": dict(int_limbs=True)}
+form_param = pytest.mark.parametrize("form", list(FORMS))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -45,26 +51,44 @@ SIZES = [1, 2, 7, 8, 9, 255, 256, 257, 511, 512, 513, 4095, 4096, 4097, 65536 + 
 
 
 @pytest.mark.parametrize("n", SIZES)
-def test_sizes(n):
-    check(si.generate("uniform11", n, seed=n), f"n={n}")
+@form_param
+def test_sizes(n, form):
+    check(si.generate("uniform11", n, seed=n), f"n={n}", **FORMS[form])
 
 
 @pytest.mark.parametrize("block", [64, 128, 256, 1024])
 @pytest.mark.parametrize("r", [1, 2, 3, 4, 5, 8])
-def test_every_configuration_gives_the_oracle_bits(block, r):
+@form_param
+def test_every_configuration_gives_the_oracle_bits(block, r, form):
     n = (1 << 20) + 4099
     x = si.generate("logu_signed", n, seed=3)
     for extra in (dict(), dict(grid_blocks=5), dict(cached_loads=True)):
-        check(x, f"block={block} r={r}", block_threads=block, chain_r=r, **extra)
+        check(x, f"block={block} r={r}", block_threads=block, chain_r=r, **extra,
+              **FORMS[form])
 
 
 @pytest.mark.parametrize("dist", ["uniform01", "uniform11", "normal", "logu_signed",
                                   "bits_finite", "alternating", "ones", "ramp2048"])
-def test_distributions(dist):
-    check(si.generate(dist, (1 << 21) + 5, seed=91), dist)
+@form_param
+def test_distributions(dist, form):
+    check(si.generate(dist, (1 << 21) + 5, seed=91), dist, **FORMS[form])
 
 
-def test_rounding_ties_and_near_ties():
+@form_param
+def test_every_binary16_value(form):
+    # every finite pattern: all together, in blocks of 4096, and each one
+    # beside its negation's neighbour (so every digit position carries)
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    vals = pats[((pats >> 10) & 31) != 31].astype(np.uint16).view(np.float16)
+    check(vals, "all finite patterns", **FORMS[form])
+    for k in range(0, vals.size, 4096):
+        check(vals[k:k + 4096], f"patterns {k}..", **FORMS[form])
+    pair = np.stack([vals, np.roll(vals, 1)], axis=1).reshape(-1)
+    check(pair[::3].copy(), "pairs", **FORMS[form])
+
+
+@form_param
+def test_rounding_ties_and_near_ties(form):
     # ties go to the even neighbour; one unit past a tie goes up
     cases = [
         ([1.0, 2.0 ** -24], 1.0),                                  # tie, 1 is even
@@ -80,28 +104,31 @@ def test_rounding_ties_and_near_ties():
     for vals, want in cases:
         x = np.array(vals, np.float16)
         assert [float(v) for v in x] == vals      # every value is binary16-exact
-        got, q = run(to_dev(x))
+        got, q = run(to_dev(x), **FORMS[form])
         assert float(got) == want, (vals, float(got), want)
         assert bits32(got) == bits32(exact_sum(x).f32)
         # the same values spread over many chains and blocks, with zeros between
         y = np.zeros(3 * (1 << 20) + 11, np.float16)
         y[np.linspace(0, y.size - 1, len(vals)).astype(np.int64)] = x
-        got, _ = run(to_dev(y))
+        got, _ = run(to_dev(y), **FORMS[form])
         assert float(got) == want, ("spread", vals, float(got))
 
 
-def test_zero_results_are_positive():
-    z, q = run(torch.empty(0, dtype=torch.float16, device="cuda"))
+@form_param
+def test_zero_results_are_positive(form):
+    kw = FORMS[form]
+    z, q = run(torch.empty(0, dtype=torch.float16, device="cuda"), **kw)
     assert bits32(z) == 0 and q == 0
     x = np.full(5000, -0.0, np.float16)
-    z, q = run(to_dev(x))
+    z, q = run(to_dev(x), **kw)
     assert bits32(z) == 0 and q == 0
     y = si.generate("uniform11", 100_001, seed=2)
-    z, q = run(to_dev(np.concatenate([y, -y])))
+    z, q = run(to_dev(np.concatenate([y, -y])), **kw)
     assert bits32(z) == 0 and q == 0
 
 
-def test_non_finite():
+@form_param
+def test_non_finite(form):
     x = si.generate("uniform11", 300_000, seed=3)
     for pos, vals in [((17,), (np.inf,)), ((299_999,), (-np.inf,)),
                       ((5, 200_000), (np.inf, -np.inf)), ((6, 7), (np.inf, -np.inf)),
@@ -110,7 +137,7 @@ def test_non_finite():
         for p, v in zip(pos, vals):
             y[p] = v
         e = exact_sum(y)
-        got, q = run(to_dev(y))
+        got, q = run(to_dev(y), **FORMS[form])
         if e.special == "nan":
             assert math.isnan(float(got)), pos
         else:
@@ -118,12 +145,14 @@ def test_non_finite():
         assert q == 0
 
 
-def test_limb_carries_and_128_bit_totals():
+@form_param
+def test_limb_carries_and_128_bit_totals(form):
+    kw = FORMS[form]
     # |sum| 2^24 beyond 2^64: the high word of the 128-bit count is in use
     n = 1 << 26
     for v in (65504.0, -65504.0):
         xd = torch.full((n,), v, dtype=torch.float16, device="cuda")
-        got, q = run(xd)
+        got, q = run(xd, **kw)
         want_q = int(v) * n * (1 << 24)
         assert q == want_q and abs(q) >= 1 << 64
         assert float(got) == v * n
@@ -131,7 +160,7 @@ def test_limb_carries_and_128_bit_totals():
     y = np.full((1 << 22) + 3, 2.0 ** -24, np.float16)
     y[123] = 65504.0
     y[4_000_000] = -65504.0
-    check(y, "carries")
+    check(y, "carries", **kw)
 
 
 def test_concurrent_streams_and_workspace_reuse():
@@ -156,7 +185,8 @@ def test_full_2p28_uniform11():
     x = si.workload("sum_2p28_u11")
     xd = to_dev(x)
     e = exact_sum(x)
-    for cfg in (dict(), dict(chain_r=4, block_threads=256), dict(cached_loads=True)):
+    for cfg in (dict(), dict(chain_r=4, block_threads=256), dict(cached_loads=True),
+                dict(int_limbs=True), dict(int_limbs=True, chain_r=2, block_threads=1024)):
         got, q = run(xd, **cfg)
         assert bits32(got) == bits32(e.f32) and q == e.q, cfg
     print(f"2^28 exact: {float(got)!r} (Q = {q})")
@@ -167,6 +197,7 @@ def test_full_2p30_logu():
     e = exact_sum(x)
     xd = to_dev(x)
     del x
-    got, q = run(xd)
-    assert bits32(got) == bits32(e.f32) and q == e.q
+    for cfg in (dict(), dict(int_limbs=True)):
+        got, q = run(xd, **cfg)
+        assert bits32(got) == bits32(e.f32) and q == e.q, cfg
     print(f"2^30 logu exact: {float(got)!r} (oracle {float(e.f32)!r})")
