@@ -8,6 +8,8 @@ wavefront or summed by a block, ragged rows and pitches, non-finite values,
 and batch invariance -- the balanced-tree reproducibility of "Taming Bitwise
 Behavior in GPU Kernels with Tensor Core" (arXiv 2609.11356, Abstract) with
 tensor-core leaves."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -163,14 +165,20 @@ def test_differs_from_the_valu_tree_but_stays_close():
 
 
 @pytest.mark.parametrize("rows,cols", [(1 << 22, 64), (268435, 1000)])
-def test_full_size_matrices_on_sampled_rows(rows, cols):
-    # the row workloads of the benchmark, in its launch configuration; the
-    # oracle checks a sample of rows spread over the matrix (a row's bits
-    # depend on that row alone)
+def test_full_size_matrices_every_row(rows, cols):
+    # the row workloads of the benchmark, in its launch configuration, every
+    # row against the oracle; the oracle runs on batches of rows in threads
+    # (rows are independent, and numpy releases the interpreter lock)
+    from concurrent.futures import ThreadPoolExecutor
     x = si.generate_rows("uniform11", rows, cols, seed=cols)
     xd = torch.from_numpy(x).to("cuda")
     got = mma_rows(xd)
-    idx = np.unique(np.concatenate([np.arange(64), np.arange(rows - 64, rows),
-                                    np.random.default_rng(cols).integers(0, rows, 4000)]))
-    want = fixed_tree_row_sums_mma_leaves(x[idx])
-    assert np.array_equal(bits(got[idx]), bits(want))
+    del xd
+    step = 32768
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(threads) as pool:
+        parts = list(pool.map(lambda r0: fixed_tree_row_sums_mma_leaves(x[r0:r0 + step]),
+                              range(0, rows, step)))
+    want = np.concatenate(parts)
+    bad = np.flatnonzero(bits(got) != bits(want))
+    assert bad.size == 0, (rows, cols, bad[:10])

@@ -13,7 +13,7 @@ import torch
 
 import arithmetic_reduction_matrix_amd as armx
 import synth_inputs as si
-from oracle import exact_row_sums, fixed_tree_row_sums
+from oracle import exact_row_sums, fixed_tree_row_sums, fixed_tree_row_sums_mma_leaves
 
 from _parity import NAN16, INF16, check_free_order, require_gpu, strided
 
@@ -134,3 +134,36 @@ def test_large_matrices(rows, cols):
     for fn in (armx.reduce_rows, armx.reduce_rows_fixed_order):
         got = fn(xd).cpu().numpy()
         assert np.array_equal(bits(got), bits(want)), (fn.__name__, rows, cols)
+
+
+@pytest.mark.parametrize("cols", [8, 33, 64, 100, 512])
+@pytest.mark.parametrize("grid_blocks", [1, 3])
+def test_many_steps_per_wavefront(cols, grid_blocks):
+    # few wavefronts and many rows: every wavefront runs many steps of its
+    # pipeline, and the last one a partial step
+    rows = 60_007 if cols <= 64 else 30_001
+    x = si.generate_rows("logu_signed", rows, cols, seed=cols + grid_blocks)
+    ld = (cols + 7) // 8 * 8
+    xd = strided(x, ld)
+    want = fixed_tree_row_sums(x)
+    for fn in (armx.reduce_rows_fixed_order, armx.reduce_rows):
+        got = fn(xd, grid_blocks=grid_blocks).cpu().numpy()
+        assert np.array_equal(bits(got), bits(want)), (fn.__name__, cols, grid_blocks)
+    got = armx.reduce_rows_fixed_order(xd, grid_blocks=grid_blocks, mma_leaves=True)
+    want = fixed_tree_row_sums_mma_leaves(x)
+    assert np.array_equal(bits(got.cpu().numpy()), bits(want)), ("mma leaves", cols)
+
+
+@pytest.mark.parametrize("cols", [8, 64, 257])
+def test_output_not_16_byte_aligned(cols):
+    # results written through an output view at an odd 4-byte offset, with
+    # guard values around it left untouched
+    rows = 20_011
+    x = si.generate_rows("normal", rows, cols, seed=cols)
+    xd = strided(x, (cols + 7) // 8 * 8)
+    buf = torch.full((rows + 5,), 12345.0, dtype=torch.float32, device="cuda")
+    out = buf[1:rows + 1]
+    armx.reduce_rows_fixed_order(xd, out=out)
+    host = buf.cpu().numpy()
+    assert np.array_equal(bits(host[1:rows + 1]), bits(fixed_tree_row_sums(x)))
+    assert host[0] == 12345.0 and (host[rows + 1:] == 12345.0).all()
