@@ -66,3 +66,34 @@ def test_noalloc_large_and_empty():
         armx.reduce_sum(y).cpu().numpy())
     big = torch.empty(1 << 28, dtype=torch.float16, device="cuda")
     assert _noalloc(big, out, one_chain=True, block_threads=64, chain_r=1) == -4
+
+
+def test_noalloc_inside_a_captured_graph():
+    # the callers it is for: code under HIP graph capture.  The call is
+    # captured (its counter clear is a kernel, not a memset), replayed on
+    # new data with eager work and synchronisations between the replays, and
+    # every replay is checked against an eager reduce_sum of the same data.
+    n = (1 << 22) + 5
+    pool = [to_dev(si.generate("uniform11", n, seed=300 + i)) for i in range(4)]
+    x = torch.empty_like(pool[0])
+    out = torch.empty(1, dtype=torch.float32, device="cuda")
+    x.copy_(pool[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        assert _noalloc(x, out) == 0          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st = _noalloc(x, out)
+    assert st == 0
+    for i in range(1, 4):
+        x.copy_(pool[i])
+        g.replay()
+        torch.cuda.synchronize()
+        want = armx.reduce_sum(pool[i]).cpu().numpy()
+        assert bits32(out.cpu().numpy()[0]) == bits32(want), i
+        # eager calls of both entry points between replays
+        assert _noalloc(pool[i - 1], torch.empty(1, device="cuda")) == 0
+        torch.cuda.synchronize()
