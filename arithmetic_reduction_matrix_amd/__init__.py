@@ -50,6 +50,9 @@ FLAG_MMA_LEVELS = 0x10
 FLAG_MMA_LEAVES = 0x20
 FLAG_ALL_ONES = 0x40
 FLAG_INT_LIMBS = 0x80
+# the counter region at the start of every non-empty workspace (zero before
+# first use; every call leaves it zero)
+COUNTER_BYTES = 65536
 
 _STATUS = {
     0: "ARMX_OK", -1: "ARMX_ERR_NULL", -2: "ARMX_ERR_ALIGN", -3: "ARMX_ERR_CONFIG",

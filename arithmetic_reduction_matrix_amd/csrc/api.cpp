@@ -143,10 +143,15 @@ int reduce_sum_noalloc(const void* x, size_t n, float* out, const armx_config* c
   void* ws = nullptr;
   if (plan.ws_bytes > 0) {
     if (armx::scratch_address(&ws) != hipSuccess) return ARMX_ERR_HIP;
-    // the completion counters must start at zero: cleared by a small kernel
-    // on the caller's stream (capturable; no memset, no allocation)
-    const hipError_t e =
-        armx::launch_zero(static_cast<float*>(ws), armx::kCounterBytes / sizeof(float), s);
+    // the completion counters the plan uses (the top counter and one per
+    // group, each kCounterStride words apart) must start at zero: cleared by
+    // a small kernel on the caller's stream (capturable; no memset, no
+    // allocation)
+    const uint64_t groups = plan.group ? (uint64_t(plan.grid) + plan.group - 1) / plan.group : 0;
+    const uint64_t words = (1 + groups) * armx::kCounterStride;
+    const hipError_t e = armx::launch_zero(
+        static_cast<float*>(ws),
+        size_t(words < armx::kCounterBytes / 4 ? words : armx::kCounterBytes / 4), s);
     if (e != hipSuccess) return ARMX_ERR_HIP;
   }
   if (plan.flags & ARMX_FLAG_MMA_LEVELS)
@@ -274,6 +279,6 @@ const char* armx_status_string(int status) {
   }
 }
 
-int armx_version(void) { return 7; }
+int armx_version(void) { return 8; }
 
 }  // extern "C"

@@ -597,14 +597,17 @@ __device__ inline void combine_split_rows(const float* parts, uint64_t rows, uns
 
 // Two-level completion.  Blocks form groups of `group` consecutive blocks (a
 // power of two, at most kTicketGroups groups); each group has its own counter
-// and the groups a top counter, so no counter sees more than a few dozen
-// increments and the atomics of different groups proceed in parallel.  The
+// and the groups a top counter, so that no counter sees many increments and
+// the atomics of different groups proceed in parallel: each counter sits in
+// its own 256-byte stretch of the workspace (kTicketStride words), since
+// device atomics on counters that share one are served one at a time.  The
 // last block of a group combines the group's block results (in index order)
 // into a group result; the last group combines the group results into out[0].
 // `combine(values, count, red)` runs on every thread of the block and returns
 // the combined value in thread 0.  Workspace: counters[0] is the top counter,
-// counters[1 + g] group g's; all start (and end) at zero.
-constexpr unsigned kTicketGroups = 63;
+// counters[(1 + g) kTicketStride] group g's; all start (and end) at zero.
+constexpr unsigned kTicketGroups = 255;
+constexpr unsigned kTicketStride = 64;
 
 template <class Combine>
 __device__ __forceinline__ void finish_two_level(float value, unsigned* counters,
@@ -615,7 +618,8 @@ __device__ __forceinline__ void finish_two_level(float value, unsigned* counters
   const unsigned g = b / group, g0 = g * group;
   const unsigned in_group = G - g0 < group ? G - g0 : group;
   const unsigned groups = (G + group - 1) / group;
-  if (!publish_and_check_last(partials + b, value, counters + 1 + g, in_group, flag)) return;
+  if (!publish_and_check_last(partials + b, value, counters + (1 + g) * kTicketStride,
+                              in_group, flag)) return;
   const float gv = combine(partials + g0, in_group, red);
   if (groups == 1) {
     if (threadIdx.x == 0) out[0] = gv;

@@ -411,7 +411,7 @@ __global__ __launch_bounds__(LIMBS ? kExactLimbsMaxBlock : 1024) void exact_kern
   const unsigned in_group = G - g0 < group ? G - g0 : group;
   const unsigned groups = (G + group - 1) / group;
   if (!publish_with_ticket([&] { store_record(partials + uint64_t(b) * kRecordWords, block_total); },
-                           counters + 1 + g, in_group, &flag))
+                           counters + (1 + g) * kTicketStride, in_group, &flag))
     return;
   const Exact gv = combine_records(partials + uint64_t(g0) * kRecordWords, in_group, lds);
   if (groups == 1) {

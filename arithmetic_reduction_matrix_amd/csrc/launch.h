@@ -9,9 +9,9 @@
 
 namespace armx {
 
-// Workspace layout of the reductions with a completion ticket: a 256-byte
-// counter region (top counter, then one per group of blocks), the block
-// results, then the group results.
+// Workspace layout of the reductions with a completion ticket: the counter
+// region (kCounterBytes: the top counter, then one per group of blocks, each
+// in its own 256-byte stretch), the block results, then the group results.
 struct Workspace {
   unsigned* counters;
   float* partials;

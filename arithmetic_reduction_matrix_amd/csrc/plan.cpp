@@ -146,9 +146,11 @@ int rows_remap(uint64_t rows, uint64_t ld) { return rows > 1 && ld % 64 != 0 ? 1
 // the kernel then has the fewest serialised memory round trips (measured
 // faster at 256 blocks).  Larger grids use a power-of-two group size near
 // sqrt(grid), so that neither a group counter nor the top counter sees many
-// increments (measured faster at 32768 blocks), with at most kMaxGroups
-// groups.  Sets the workspace sizes.
-constexpr uint64_t kSingleLevelMax = 1024;
+// increments, with at most kMaxGroups groups (measured on MI355X, 2^28
+// values, 64-thread blocks: at R = 4, 1024 blocks, 86.0 us in one group and
+// 76.9 us in 32; one chain per wavefront at R = 1, 2^19 blocks, 1848 us in 63
+// groups and 619 us in 255).  Sets the workspace sizes.
+constexpr uint64_t kSingleLevelMax = 256;
 
 void size_ticket(Plan& p, size_t record_bytes = sizeof(float)) {
   const uint64_t G = uint64_t(p.grid);

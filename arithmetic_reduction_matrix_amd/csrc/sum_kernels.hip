@@ -41,6 +41,9 @@ namespace {
 
 using namespace dev;
 
+static_assert(kTicketGroups == kMaxGroups && kTicketStride == kCounterStride,
+              "the kernels' ticket layout is the plan's workspace layout");
+
 // Reduces partials[0..count) in a fixed order with one block; valid in thread 0.
 __device__ float reduce_partials(const float* partials, unsigned count, float* red) {
   float s = 0.0f;

@@ -32,10 +32,10 @@
  *   stderr.  A failure reported by the HIP runtime while enqueueing returns
  *   ARMX_ERR_HIP.
  * - Workspace: `ws` points to at least armx_workspace_bytes(...) bytes,
- *   256-byte aligned.  Its first 256 bytes hold a completion counter that
- *   MUST be zero before the first call that uses the buffer; every call
- *   leaves it zero again when it completes, so zero-filling a workspace once
- *   after allocating it is enough.  Calls that may run at the same time
+ *   256-byte aligned.  Its first ARMX_COUNTER_BYTES bytes hold the
+ *   completion counters, which MUST be zero before the first call that uses
+ *   the buffer; every call leaves them zero again when it completes, so
+ *   zero-filling a workspace once after allocating it is enough.  Calls that may run at the same time
  *   (different streams) need different workspaces.  When the required size
  *   is 0, ws may be NULL.
  * - Non-finite inputs follow IEEE addition: any NaN, or +Inf together with
@@ -52,6 +52,12 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Size of the counter region at the start of every non-empty workspace: a
+ * top counter and up to 255 group counters, each at the start of its own
+ * 256 bytes (device atomics on counters that share 256 bytes are served one
+ * at a time). */
+#define ARMX_COUNTER_BYTES 65536u
 
 typedef enum armx_status {
   ARMX_OK = 0,
@@ -340,8 +346,8 @@ int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, vo
  * reduce_sum with the same n, configuration and device), but the counter
  * region and block results live in a static device array of the library, 1
  * MiB per GPU, reserved when the library is loaded and held until the
- * process ends.  Each call first clears the array's 256-byte counter region
- * with a small kernel on `stream`, then launches reduce_sum's kernels on it;
+ * process ends.  Each call first clears the counters its plan uses (a
+ * 256-byte stretch per counter) with a small kernel on `stream`, then launches reduce_sum's kernels on it;
  * it calls no hipMalloc, hipFree or other allocating routine.  On its first
  * call on a device it looks up the array's device address
  * (hipGetSymbolAddress) with that device current.
@@ -410,7 +416,7 @@ int armx_launch_plan(int op, size_t n_or_rows, size_t cols, const armx_config* c
 /* armx_status_string -- a static, human-readable name for a status code. */
 const char* armx_status_string(int status);
 
-/* armx_version -- ABI version of this header: 7. */
+/* armx_version -- ABI version of this header: 8. */
 int armx_version(void);
 
 #ifdef __cplusplus

@@ -38,7 +38,7 @@ static int failures = 0;
 static int cpu_checks(void) {
   char* fake = (char*)(uintptr_t)(1u << 20); /* never dereferenced */
   armx_config bad = {96, 0, 0, 0, NULL, NULL};
-  EXPECT(armx_version() == 7);
+  EXPECT(armx_version() == 8);
   {
     armx_plan_info info;
     EXPECT(armx_launch_plan(ARMX_OP_FIXED, (size_t)1 << 26, 0, NULL, &info) == ARMX_OK);

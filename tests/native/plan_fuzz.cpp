@@ -210,7 +210,9 @@ int main(int argc, char** argv) {
       EXPECT(p.grid >= 1, "grid %d", p.grid);
       EXPECT(pow2(p.group), "group %u", p.group);
       EXPECT(cdiv(uint64_t(p.grid), p.group) <= armx::kMaxGroups, "groups");
-      EXPECT(p.ws_bytes == armx::kCounterBytes + p.partials_bytes + 256, "ws layout");
+      EXPECT(p.ws_bytes == armx::kCounterBytes + p.partials_bytes +
+                             (4 * armx::kMaxGroups + 255) / 256 * 256,
+             "ws layout");
       EXPECT(p.partials_bytes >= 4 * uint64_t(p.grid) && p.partials_bytes % 256 == 0, "partials");
     }
     if (op == ARMX_OP_SUM) {

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert armx.lib.armx_version() == 7
+    assert armx.lib.armx_version() == 8
     for st in range(0, -7, -1):
         s = armx.lib.armx_status_string(st).decode()
         assert s.startswith("ARMX_")
@@ -134,9 +134,9 @@ def test_exact_argument_errors():
 
 
 def test_exact_workspace_sizes():
-    # counter region + 32-byte records per block + 63 group records
+    # counter region + 32-byte records per block + 255 group records
     def ws(grid):
-        return 256 + (32 * grid + 255) // 256 * 256 + 2048
+        return armx.COUNTER_BYTES + (32 * grid + 255) // 256 * 256 + 8192
     assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28) == ws(256)
     assert armx.workspace_bytes(armx.OP_EXACT, 1 << 28, block_threads=64) == ws(512)
     assert armx.workspace_bytes(armx.OP_EXACT, 1000) == ws(1)
@@ -195,10 +195,10 @@ def test_mma_levels_workspace_sizes():
     for n, r in ((1 << 28, 8), (1 << 28, 1), ((1 << 20) + 1, 4), (3000, 1)):
         c1 = -(-n // (512 * r))
         c2 = -(-c1 // (256 * r))
-        want = 256 + r256(4 * c1) + (r256(4 * c2) if c2 > 1 else 0)
+        want = armx.COUNTER_BYTES + r256(4 * c1) + (r256(4 * c2) if c2 > 1 else 0)
         assert armx.workspace_bytes(armx.OP_SUM, n, chain_r=r, mma_levels=True) == want, (n, r)
     assert armx.workspace_bytes(armx.OP_SUM, 4096, chain_r=8, mma_levels=True) == 0
-    assert armx.workspace_bytes(armx.OP_SUM, 4097, chain_r=8, mma_levels=True) == 256 + 256
+    assert armx.workspace_bytes(armx.OP_SUM, 4097, chain_r=8, mma_levels=True) == armx.COUNTER_BYTES + 256
     # the grid does not change the level buffers
     assert (armx.workspace_bytes(armx.OP_SUM, 1 << 24, mma_levels=True, block_threads=1024)
             == armx.workspace_bytes(armx.OP_SUM, 1 << 24, mma_levels=True, one_chain=True))
@@ -251,10 +251,13 @@ def test_rows_fixed_argument_errors():
 
 
 def test_workspace_sizes():
-    # layout: 256-byte counter region + block results (rounded to 256 bytes)
-    # + 256 bytes of group results
+    # layout: the counter region (a top counter and 255 group counters, 256
+    # bytes apart) + block results (rounded to 256 bytes) + 1024 bytes of
+    # group results
+    assert armx.COUNTER_BYTES == 256 * 256
+
     def ws(grid):
-        return 256 + (4 * grid + 255) // 256 * 256 + 256
+        return armx.COUNTER_BYTES + (4 * grid + 255) // 256 * 256 + 1024
     # persistent grid: 256 CUs x 2 waves / 2 waves per block = 256 blocks
     n = 1 << 28
     assert armx.workspace_bytes(armx.OP_SUM, n) == ws(256)
@@ -272,8 +275,8 @@ def test_workspace_sizes():
     # region + one partial per wavefront (256 CUs, R = 8: 512 wavefronts, so
     # one row of 2^28 values in 512 parts); the pitch does not matter, so a
     # ragged width is accepted by the query
-    assert armx.workspace_bytes(armx.OP_ROWS, 1, 1 << 28) == 256 + 4 * 512
-    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 1, 1 << 28) == 256 + 4 * 512
+    assert armx.workspace_bytes(armx.OP_ROWS, 1, 1 << 28) == armx.COUNTER_BYTES + 4 * 512
+    assert armx.workspace_bytes(armx.OP_ROWS_FIXED, 1, 1 << 28) == armx.COUNTER_BYTES + 4 * 512
     assert armx.workspace_bytes(armx.OP_ROWS, 4, 100_003) > 0
     assert armx.workspace_bytes(armx.OP_ROWS, 3, 4096) == 0   # too short to split
     # fixed order, n = 2^26: 2^17 chunks; 256 CUs x 16/8 waves -> 256 blocks

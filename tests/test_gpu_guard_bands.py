@@ -76,7 +76,7 @@ def test_flat_entry_points_stay_in_bounds(n, name, op, cfg):
     assert out.guards_intact() and ws.guards_intact() and fixed.guards_intact(), (name, n)
     assert bool((ws.body()[need:] == PATTERN).all().item()), (name, n, "workspace tail")
     if need:   # the ticket paths restore their counters; the levels form never touches them
-        assert int(ws.body()[:256].count_nonzero().item()) == 0, (name, n, "counter region")
+        assert int(ws.body()[:armx.COUNTER_BYTES].count_nonzero().item()) == 0, (name, n, "counter region")
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 700), (300, 4096), (4097, 2048 + 8)])
@@ -124,4 +124,4 @@ def test_split_rows_stay_in_bounds(rows, cols, fixed_order, mma_leaves):
     assert torch.equal(first, second)
     assert out.guards_intact() and ws.guards_intact(), (rows, cols)
     assert bool((ws.body()[need:] == PATTERN).all().item()), (rows, cols, "workspace tail")
-    assert int(ws.body()[:256].count_nonzero().item()) == 0, (rows, cols, "counter region")
+    assert int(ws.body()[:armx.COUNTER_BYTES].count_nonzero().item()) == 0, (rows, cols, "counter region")
