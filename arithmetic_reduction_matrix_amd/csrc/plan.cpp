@@ -79,21 +79,40 @@ uint64_t cap_small_input(uint64_t blocks, uint64_t n, const OpDefaults& d, int c
 }
 
 // Rows of at most one chunk (mode 2): a row takes ceil(cols / 8) lanes,
-// padded to a power of two.  Sets the mode, the lane count and the grid.
+// padded to a power of two.  Staged widths: the rows (all but a last row
+// whose width is not a multiple of 8, which one wavefront sums apart) are cut
+// into chunks of whole steps, about one per block of the persistent grid and
+// at most kShortChunkRows rows, which the blocks take in turn.  Sets the mode,
+// the lane count, the groups per step (r), the grid and, when staged, the
+// chunk and its LDS.
 void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
   const uint64_t lanes = (p.n + 7) / 8;
   int lg = 0;
   while ((uint64_t(1) << lg) < lanes) ++lg;
   p.mode = 2;
   p.seg_log2 = lg;
-  const uint64_t rows_per_group = uint64_t(64) >> lg;
-  const uint64_t groups = (p.rows + rows_per_group - 1) / rows_per_group;
-  const uint64_t waves = (groups + kShortGroups - 1) / kShortGroups;
-  uint64_t grid = (waves + W - 1) / W;
-  const uint64_t resident = ceil_div(uint64_t(cu_count) * kShortWavesPerCu, W);
-  if (grid > resident) grid = resident;
-  if (grid_cap > 0 && grid > uint64_t(grid_cap)) grid = uint64_t(grid_cap);
+  const bool staged = lg >= kShortStagedMinLog2;
+  p.r = staged && (p.rows == 1 || p.ld % 64 == 0) ? 4 : 8;   // groups per step
+  const uint64_t rows_per_step = (uint64_t(64) >> lg) * uint64_t(p.r);
+  uint64_t target = ceil_div(uint64_t(cu_count) * kShortWavesPerCu, W);
+  if (grid_cap > 0 && target > uint64_t(grid_cap)) target = uint64_t(grid_cap);
+  if (!staged) {
+    const uint64_t waves = ceil_div(p.rows, rows_per_step);
+    const uint64_t grid = ceil_div(waves, W);
+    p.grid = int(grid < 1 ? 1 : (grid < target ? grid : target));
+    p.chunk_rows = 0;
+    p.lds_bytes = 0;
+    return;
+  }
+  const uint64_t body = p.rows - (p.n % 8 ? 1 : 0);
+  uint64_t per_chunk = ceil_div(ceil_div(body, rows_per_step), target);
+  if (per_chunk < 1) per_chunk = 1;
+  if (per_chunk > kShortChunkRows / rows_per_step) per_chunk = kShortChunkRows / rows_per_step;
+  p.chunk_rows = per_chunk * rows_per_step;
+  const uint64_t chunks = ceil_div(body, p.chunk_rows);
+  const uint64_t grid = chunks < target ? chunks : target;
   p.grid = int(grid < 1 ? 1 : grid);
+  p.lds_bytes = size_t(p.chunk_rows) * sizeof(float);
 }
 
 // Automatic shapes for rows longer than one chunk (cols > 512), measured on

@@ -100,6 +100,7 @@ struct Plan {
   uint64_t n = 0;           // elements (sum / fixed); columns (rows)
   uint64_t rows = 0;
   uint64_t ld = 0;
+  uint64_t chunk_rows = 0;  // mode 2: rows a block reduces into LDS before writing them
   size_t ws_bytes = 0;      // workspace the launch needs
   size_t partials_bytes = 0;  // block-result region of the workspace (MMA levels:
                               // the first level buffer)
@@ -115,14 +116,27 @@ struct Plan {
 constexpr uint64_t kPaceLongChains = 64;
 constexpr uint64_t kPaceShortChains = 8;
 
-// Rows of at most one chunk (mode 2): each wavefront takes kShortGroups
-// groups of 64 / 2^seg_log2 rows per step, one 16-byte load per lane each,
-// and the persistent grid holds kShortWavesPerCu wavefronts per compute unit
-// (measured on MI355X at 2^28 values: 4 beat 2 and 8 for 64 to 512 columns,
-// best as one block of 4 wavefronts).
-constexpr int kShortGroups = 8;
+// Rows of at most one chunk (mode 2): each wavefront takes G groups of
+// 64 / 2^S rows per step (S = seg_log2, G = the plan's r), one 16-byte load
+// per lane each, and the persistent grid holds kShortWavesPerCu wavefronts
+// per compute unit (measured on MI355X at 2^28 values: 4 beat 2 and 8 for 64
+// to 512 columns, best as one block of 4 wavefronts).
+//  * Rows of more than 32 values (S >= kShortStagedMinLog2) are cut into
+//    chunks of at most kShortChunkRows consecutive rows; a block reduces a
+//    chunk into LDS and writes the chunk's sums out together (4194304 rows of
+//    64 values: 87.4 -> 80.6 us against every wavefront storing its sums step
+//    by step; 128 to 512 values 1-6 us faster).  G = 4 when the row pitch is
+//    a whole number of 128-byte lines, else 8 (2581110 rows of 100 values at
+//    a pitch of 104: 83.3 us at G = 4 against 81.4 at G = 8, and 91.0 against
+//    81.1 with MFMA leaves; at a pitch of 64, 80.6 against 83.4).
+//  * Narrower rows write as they go, G = 8: their sums are 1/8 to 1/2 of the
+//    input bytes, more than a chunk of LDS holds for the grid to stream on
+//    while it is written out (33554432 rows of 8 values: 104.7 us writing as
+//    they go, 116-125 us through LDS).
 constexpr int kShortWavesPerCu = 4;
 constexpr int kShortBlock = 256;   // automatic block size for such rows
+constexpr int kShortStagedMinLog2 = 3;
+constexpr uint64_t kShortChunkRows = 16384;   // 64 KiB of LDS
 // Largest block of the MFMA-leaf kernel for such rows: its two reduction
 // paths need more than the 128 registers a 1024-thread block leaves a lane
 // (a larger requested block is lowered to this; a row's result never depends

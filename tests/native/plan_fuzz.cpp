@@ -44,10 +44,10 @@ int main(int argc, char** argv) {
       uint64_t rows, cols, ld;
       int mode, seg_log2, waves, r, remap;
     } cases[] = {
-        {ARMX_OP_ROWS, 100000, 64, 64, 2, 3, 4, -1, 0},
-        {ARMX_OP_ROWS_FIXED, 100000, 100, 104, 2, 4, 4, -1, 1},
-        {ARMX_OP_ROWS, 100000, 8, 8, 2, 0, 4, -1, 1},
-        {ARMX_OP_ROWS, 100000, 512, 512, 2, 6, 4, -1, 0},
+        {ARMX_OP_ROWS, 100000, 64, 64, 2, 3, 4, 4, 0},          // r: groups per step
+        {ARMX_OP_ROWS_FIXED, 100000, 100, 104, 2, 4, 4, 8, 1},
+        {ARMX_OP_ROWS, 100000, 8, 8, 2, 0, 4, 8, 1},
+        {ARMX_OP_ROWS, 100000, 512, 512, 2, 6, 4, 4, 0},
         {ARMX_OP_ROWS, 300000, 1000, 1000, 1, 0, 8, 1, 1},
         {ARMX_OP_ROWS_FIXED, 300000, 1000, 1000, 1, 0, 4, 1, 1},
         {ARMX_OP_ROWS_FIXED, 300000, 1024, 1024, 1, 0, 8, 2, 0},
@@ -302,9 +302,27 @@ int main(int argc, char** argv) {
         const uint64_t lanes = cdiv(p.n, 8), P = uint64_t(1) << p.seg_log2;
         EXPECT(p.seg_log2 >= 0 && p.seg_log2 <= 6, "seg_log2 %d", p.seg_log2);
         EXPECT(P >= lanes && (P == 1 || P / 2 < lanes), "lanes per row");
-        const uint64_t steps = cdiv(p.rows, (64 / P) * armx::kShortGroups);
-        EXPECT(uint64_t(p.grid) <= cdiv(steps, W), "short-row grid %d", p.grid);
-        EXPECT(p.lds_bytes == 0, "short-row lds");
+        // 4 groups per step for staged rows at a whole-line pitch, else 8
+        EXPECT(p.r == (p.seg_log2 >= armx::kShortStagedMinLog2 && (p.rows == 1 || p.ld % 64 == 0)
+                           ? 4 : 8),
+               "short-row groups %d", p.r);
+        const uint64_t rps = (64 / P) * uint64_t(p.r);
+        const uint64_t steps = cdiv(p.rows, rps);
+        EXPECT(c.grid_blocks <= 0 || p.grid <= c.grid_blocks, "short-row grid cap");
+        if (p.seg_log2 >= armx::kShortStagedMinLog2) {
+          // a chunk (a block's share) is at least one step
+          EXPECT(uint64_t(p.grid) <= steps, "short-row grid %d", p.grid);
+          // chunks of whole steps that fit the LDS, and no more blocks than chunks
+          EXPECT(p.chunk_rows >= rps && p.chunk_rows % rps == 0 &&
+                     p.chunk_rows <= armx::kShortChunkRows,
+                 "short-row chunk %llu", (unsigned long long)p.chunk_rows);
+          EXPECT(p.lds_bytes == p.chunk_rows * sizeof(float), "short-row lds");
+          const uint64_t body = p.rows - (p.n % 8 ? 1 : 0);
+          EXPECT(uint64_t(p.grid) <= (body ? cdiv(body, p.chunk_rows) : 1), "short-row chunks");
+        } else {
+          EXPECT(uint64_t(p.grid) <= cdiv(steps, W), "short-row grid %d", p.grid);
+          EXPECT(p.chunk_rows == 0 && p.lds_bytes == 0, "short-row lds");
+        }
         EXPECT(!(p.flags & ARMX_FLAG_MMA_LEAVES) || W * 64 <= armx::kShortMmaMaxBlock,
                "MFMA-leaf short-row block %llu", (unsigned long long)(W * 64));
       }
