@@ -4,12 +4,15 @@ ragged tails, several blocks and both ticket levels), the guards must be
 intact, the workspace's counter region must be back at zero, and the part of
 the workspace past what armx_workspace_bytes asks for must be untouched (also
 for few long rows, which the row entry points split over blocks with a
-workspace)."""
+workspace, and for rows of at most 512 values, whose sums a block may stage
+in LDS and write out a chunk at a time)."""
+import numpy as np
 import pytest
 import torch
 
 import arithmetic_reduction_matrix_amd as armx
 import synth_inputs as si
+from oracle import fixed_tree_row_sums, fixed_tree_row_sums_mma_leaves
 
 from _parity import require_gpu, to_dev
 
@@ -77,6 +80,32 @@ def test_flat_entry_points_stay_in_bounds(n, name, op, cfg):
     assert bool((ws.body()[need:] == PATTERN).all().item()), (name, n, "workspace tail")
     if need:   # the ticket paths restore their counters; the levels form never touches them
         assert int(ws.body()[:armx.COUNTER_BYTES].count_nonzero().item()) == 0, (name, n, "counter region")
+
+
+# rows of at most 512 values: the direct kernel (8 values) and the staged one
+# (45, 64, 100, 512 values: chunks of rows through LDS, a ragged last row for
+# 45 and 100, one block looping over several chunks with grid_blocks=2)
+_SHORT = [(1, 1, {}), (5000, 8, {}), (3001, 45, {}), (40_000, 64, {}), (20_001, 100, {}),
+          (777, 512, {}), (40_000, 64, dict(grid_blocks=2)), (20_001, 100, dict(grid_blocks=2))]
+
+
+@pytest.mark.parametrize("rows,cols,cfg", _SHORT)
+@pytest.mark.parametrize("fixed_order,mma_leaves", [(False, False), (True, False), (True, True)])
+def test_short_rows_stay_in_bounds(rows, cols, cfg, fixed_order, mma_leaves):
+    ld = (cols + 7) // 8 * 8
+    x = si.generate_rows("normal", rows, cols, seed=rows + cols)
+    buf = np.zeros((rows, ld), np.float16)
+    buf[:, :cols] = x
+    m = to_dev(buf)[:, :cols]
+    out = Guarded(4 * rows)
+    fn = armx.reduce_rows_fixed_order if fixed_order else armx.reduce_rows
+    extra = dict(mma_leaves=True) if mma_leaves else {}
+    fn(m, out=out.body(torch.float32), **cfg, **extra)
+    torch.cuda.synchronize()
+    assert out.guards_intact(), (rows, cols, cfg, fixed_order, mma_leaves)
+    got = out.body(torch.float32).cpu().numpy()
+    want = fixed_tree_row_sums_mma_leaves(x) if mma_leaves else fixed_tree_row_sums(x)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (rows, cols, cfg)
 
 
 @pytest.mark.parametrize("rows,cols", [(1, 1), (3, 700), (300, 4096), (4097, 2048 + 8)])

@@ -119,9 +119,12 @@ def test_every_binary16_value_as_a_one_value_row():
         assert np.array_equal(np.isnan(got), np.isnan(want))
 
 
-@pytest.mark.parametrize("rows,cols", [((1 << 22) + 3, 64), ((1 << 20) + 1, 250)])
+@pytest.mark.parametrize("rows,cols", [((1 << 22) + 3, 64), ((1 << 20) + 1, 250),
+                                       ((1 << 21) + 5, 100)])
 def test_large_matrices(rows, cols):
-    # at the 2^28-value scale: every row against the tree oracle
+    # at the 2^28-value scale: every row against the tree oracle (64 and 250
+    # values: whole-line pitches, 4 groups per step; 100 values at a pitch of
+    # 104: 8 groups per step and a ragged last row)
     x = si.generate_rows("uniform11", rows, cols, seed=cols)
     ld = (cols + 7) // 8 * 8
     if ld == cols:
