@@ -142,10 +142,9 @@ __device__ __forceinline__ bool has_non_finite(u32x4 t) {
 // Rows of at most 32 values (S <= 2): every wavefront of the grid takes the
 // steps in turn and stores its rows' sums as it goes, 8 groups per step.
 template <int S, bool NT, bool MMA>
-__global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_direct_kernel(const uint16_t* __restrict__ x,
-                                                          uint64_t rows, uint64_t cols,
-                                                          uint64_t ld, float* __restrict__ out,
-                                                          int remap) {
+__global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_direct_kernel(
+    const uint16_t* __restrict__ x, uint64_t rows, uint64_t cols, uint64_t ld,
+    float* __restrict__ out, int remap) {
   constexpr uint64_t P = uint64_t(1) << S;
   constexpr int G = 8;
   constexpr uint64_t RPG = 64 >> S;   // rows per group (one wavefront load)
@@ -246,10 +245,9 @@ __global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_dir
 
 // Rows of more than 32 values (S >= 3): chunks of rows staged in LDS.
 template <int S, int G, bool NT, bool MMA>
-__global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_staged_kernel(const uint16_t* __restrict__ x,
-                                                          uint64_t rows, uint64_t cols,
-                                                          uint64_t ld, float* __restrict__ out,
-                                                          uint64_t chunk_rows) {
+__global__ __launch_bounds__(MMA ? kShortMmaMaxBlock : 1024) void short_rows_staged_kernel(
+    const uint16_t* __restrict__ x, uint64_t rows, uint64_t cols, uint64_t ld,
+    float* __restrict__ out, uint64_t chunk_rows) {
   extern __shared__ float staged[];   // the chunk's sums (chunk_rows floats)
   constexpr uint64_t P = uint64_t(1) << S;
   constexpr uint64_t RPG = 64 >> S;   // rows per group (one wavefront load)
