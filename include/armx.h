@@ -125,7 +125,10 @@ typedef struct armx_config {
  * has little to stream).
  * The row entry points pick their defaults by row length: rows of at most
  * 512 values take the segmented kernel (block 256, 4 wavefronts per compute
- * unit; chain_r has no effect there); rows of 513 to 3584 values take R = 1
+ * unit, 4 or 8 loads per step -- 4 for rows of more than 32 values at a pitch
+ * of whole 128-byte lines -- which armx_launch_plan reports as chain_r;
+ * chain_r has no effect there; rows of more than 32 values use up to 64 KiB
+ * of LDS per block to hold a chunk of row sums); rows of 513 to 3584 values take R = 1
  * and blocks of 512 threads (fixed order: R = 2 or 4 and 512 threads when a
  * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
  * rows the R that leaves a row's last chain of R chunks the least padding,
