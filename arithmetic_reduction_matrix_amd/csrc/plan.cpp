@@ -96,6 +96,7 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
   const uint64_t rows_per_step = (uint64_t(64) >> lg) * uint64_t(p.r);
   uint64_t target = ceil_div(uint64_t(cu_count) * kShortWavesPerCu, W);
   if (grid_cap > 0 && target > uint64_t(grid_cap)) target = uint64_t(grid_cap);
+  if (staged) p.xcd_remap = 0;   // a chunk is one block's range of rows already
   if (!staged) {
     const uint64_t waves = ceil_div(p.rows, rows_per_step);
     const uint64_t grid = ceil_div(waves, W);
