@@ -80,8 +80,7 @@ def event_timed(torch, fn, iters: int, warmup: int = 5):
     """Average ms per call of fn(i) over `iters` back-to-back eager calls: one
     pair of events on the current stream around all of them (as for the
     headline's timed steps), so no marker packets sit between the calls; for
-    calls shorter than their host overhead this is the eager call rate.
-    Returns (average, average)."""
+    calls shorter than their host overhead this is the eager call rate."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -91,8 +90,7 @@ def event_timed(torch, fn, iters: int, warmup: int = 5):
         fn(i)
     e.record()
     torch.cuda.synchronize()
-    avg = s.elapsed_time(e) / iters
-    return avg, avg
+    return s.elapsed_time(e) / iters
 
 
 def graph_timed(torch, call, calls: int, reps: int = 5):
@@ -426,22 +424,22 @@ def main() -> int:
     stress_np = None   # the 2^30 precision-stress input, drawn with the variants
     if not args.no_variants:
         var = {}
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], plain=True), 200)
+        ms = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], plain=True), 200)
         var["plain_shuffle_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6,
                                      "vs_mfma": avg_ms / ms}
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], all_ones=True), 200)
+        ms = event_timed(torch, lambda i: armx.reduce_sum(bufs[i & 1], all_ones=True), 200)
         var["mfma_all_ones_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "vs_signed": avg_ms / ms}
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum(
+        ms = event_timed(torch, lambda i: armx.reduce_sum(
             bufs[i & 1], one_chain=True, block_threads=256, chain_r=4), 50)
         var["one_chain_b256_r4_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: bufs[i & 1].sum(dtype=torch.float32), 100)
+        ms = event_timed(torch, lambda i: bufs[i & 1].sum(dtype=torch.float32), 100)
         var["torch_sum_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1]), 200)
+        ms = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1]), 200)
         exact_val = armx.reduce_sum_exact(bufs[0]).cpu().numpy()
         var["exact_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6, "vs_free_order": avg_ms / ms,
                              "result_bits": int(exact_val.view(np.uint32))}
         # the exact sum with integer MFMAs over 8-bit limbs (ARMX_FLAG_INT_LIMBS)
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1], int_limbs=True),
+        ms = event_timed(torch, lambda i: armx.reduce_sum_exact(bufs[i & 1], int_limbs=True),
                               200)
         k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: armx.reduce_sum_exact(
             bufs[i & 1], int_limbs=True, start_event=s_ev, stop_event=e_ev))
@@ -450,7 +448,7 @@ def main() -> int:
                                        "vs_binary64_form": var["exact_2p28"]["ms"] / ms,
                                        "result_bits": int(limb_val.view(np.uint32))}
         for r in (8, 4):
-            ms, med = event_timed(torch, lambda i: armx.reduce_sum(
+            ms = event_timed(torch, lambda i: armx.reduce_sum(
                 bufs[i & 1], mma_levels=True, chain_r=r), 200)
             var[f"mma_levels_r{r}_2p28"] = {"ms": ms, "gbs": 2 * n / ms / 1e6,
                                             "launches": mma_levels_count(n, r),
@@ -479,16 +477,16 @@ def main() -> int:
             assert sout.cpu().numpy().view(np.uint32) == eager.view(np.uint32), key
             k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: fn(
                 xs[i & 1], out=sout, workspace=sws, start_event=s_ev, stop_event=e_ev, **kw))
-            e_ms, _ = event_timed(torch, lambda i: fn(xs[i & 1], out=sout, workspace=sws, **kw),
+            e_ms = event_timed(torch, lambda i: fn(xs[i & 1], out=sout, workspace=sws, **kw),
                                   200)
             var[key] = {"ms": g_ms, "gbs": 2 * (1 << 20) / g_ms / 1e6,
                         "timing": "graph of 200 back-to-back calls",
                         "kernel_ms": k_ms, "eager_call_ms": e_ms}
         del xs
         xl = torch.empty(1 << 30, dtype=torch.float16, device=dev).uniform_(-1, 1)
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum(xl), 50)
+        ms = event_timed(torch, lambda i: armx.reduce_sum(xl), 50)
         var["sum_2p30"] = {"ms": ms, "gbs": 2 * (1 << 30) / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: armx.reduce_sum_exact(xl), 50)
+        ms = event_timed(torch, lambda i: armx.reduce_sum_exact(xl), 50)
         var["exact_2p30"] = {"ms": ms, "gbs": 2 * (1 << 30) / ms / 1e6}
         del xl
 
@@ -529,7 +527,7 @@ def main() -> int:
                                200)
             k_ms = stamped_timed(torch, lambda i, s_ev, e_ev: fn(
                 fbufs[i & 3], out=fout, workspace=fws, start_event=s_ev, stop_event=e_ev, **kw))
-            e_ms, _ = event_timed(torch, lambda i: fn(fbufs[i & 3], out=fout, workspace=fws, **kw),
+            e_ms = event_timed(torch, lambda i: fn(fbufs[i & 3], out=fout, workspace=fws, **kw),
                                   200)
             var[key] = {"ms": g_ms, "gbs": 2 * xf_np.size / g_ms / 1e6,
                         "timing": "graph of 200 back-to-back calls", "kernel_ms": k_ms,
@@ -544,15 +542,15 @@ def main() -> int:
         rbufs = [torch.from_numpy(xr_np).to(dev)]
         rbufs.append(rbufs[0].clone())
         rout = torch.empty(4096, dtype=torch.float32, device=dev)
-        ms, med = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout), 200)
+        ms = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout), 200)
         var["rows_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout,
+        ms = event_timed(torch, lambda i: armx.reduce_rows(rbufs[i & 1], out=rout,
                                                                  plain=True), 100)
         var["rows_4096x65536_plain"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(rbufs[i & 1],
+        ms = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(rbufs[i & 1],
                                                                              out=rout), 200)
         var["rows_fixed_order_4096x65536"] = {"ms": ms, "gbs": 2 * xr_np.size / ms / 1e6}
-        ms, med = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(
+        ms = event_timed(torch, lambda i: armx.reduce_rows_fixed_order(
             rbufs[i & 1], out=rout, mma_leaves=True), 200)
         var["rows_fixed_order_mma_leaves_4096x65536"] = {"ms": ms,
                                                          "gbs": 2 * xr_np.size / ms / 1e6}
@@ -568,7 +566,7 @@ def main() -> int:
             for tag, fn in (("rows", armx.reduce_rows),
                             ("rows_fixed_order", armx.reduce_rows_fixed_order),
                             ("rows_fixed_order_mma_leaves", mma_rows)):
-                ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
+                ms = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
                 var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
             del views, vout
         # few long rows, each split over wavefronts of several blocks
@@ -579,7 +577,7 @@ def main() -> int:
             moved = 2 * n + 4 * nrows
             for tag, fn in (("rows", armx.reduce_rows),
                             ("rows_fixed_order", armx.reduce_rows_fixed_order)):
-                ms, med = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
+                ms = event_timed(torch, lambda i: fn(views[i & 1], out=vout), 100)
                 var[f"{tag}_{nrows}x{cols}"] = {"ms": ms, "gbs": moved / ms / 1e6}
             del views, vout
 
