@@ -24,7 +24,8 @@
  *   host is never synchronised.
  * - The caller owns every buffer.  The library allocates no memory and keeps
  *   no state between calls other than a per-device cache of the compute-unit
- *   count.
+ *   count.  Outputs and the workspace must not overlap the input or each
+ *   other (the kernels read x while results are written).
  * - Errors are returned as a negative armx_status before anything is
  *   enqueued; the library never aborts, and prints nothing unless the
  *   environment variable ARMX_LOG is set, in which case every accepted call
