@@ -123,7 +123,12 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 // (9-chunk rows at R = 8: 172 us against 77 us at R = 3).
 //  * Rows of fewer than 8 chunks carry a fixed cost per row (the chain's
 //    result, the row combine, the store) that more wavefronts hide: R = 1
-//    (16 wavefronts per compute unit) in blocks of 512 threads; fixed-order
+//    (16 wavefronts per compute unit) in blocks of 512 threads, except free-
+//    order rows of 4 or 6 chunks in matrices of at least four rounds of that
+//    stream, which take R = 2 (half the chains per row, the same loads in
+//    flight; 2600-value rows 88.0 -> 83.1 us, 2048 79.1 -> 77.7, 3072
+//    78.9 -> 77.3; 2-chunk rows lose, 79.9 -> 97.6 us, and so do small
+//    matrices, 1500 x 2048 4.1 -> 4.5 us); fixed-order
 //    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
 //    short fixed-order rows R = 1 in blocks of 256.
 //  * Longer rows: the R that pads the last chain least -- 8, 5 or 4 for
@@ -138,10 +143,15 @@ struct RowShape {
   int block;
 };
 
-RowShape rows_auto_shape(uint64_t cols, const OpDefaults& d, bool fixed) {
+RowShape rows_auto_shape(uint64_t rows, uint64_t cols, int cu_count, const OpDefaults& d,
+                         bool fixed) {
   const uint64_t chunks = ceil_div(cols, kChunk);
   if (chunks < 8) {
     if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
+    // (only with rows for four rounds of the R = 1 stream: smaller matrices
+    // are latency-bound and want the wavefronts)
+    if (!fixed && chunks >= 4 && chunks % 2 == 0 && rows >= 4 * 16 * uint64_t(cu_count))
+      return {2, 512};
     return {1, fixed ? 256 : 512};
   }
   auto waste = [&](uint64_t r) { return ceil_div(chunks, r) * r - chunks; };
@@ -335,7 +345,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     }
     uint64_t W = uint64_t(p.waves);
     if (cols > kChunk) {
-      const RowShape a = rows_auto_shape(cols, d, false);
+      const RowShape a = rows_auto_shape(rows, cols, cu_count, d, false);
       if (auto_r) R = a.r;
       if (auto_block) W = uint64_t(a.block / 64);
       p.r = int(R);
@@ -443,7 +453,7 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
     }
     uint64_t W = uint64_t(p.waves);
     {
-      const RowShape a = rows_auto_shape(cols, d, true);
+      const RowShape a = rows_auto_shape(rows, cols, cu_count, d, true);
       if (auto_r) R = a.r;
       if (auto_block) W = uint64_t(a.block / 64);
       p.r = int(R);
