@@ -130,7 +130,9 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 //    78.9 -> 77.3; 2-chunk rows lose, 79.9 -> 97.6 us, and so do small
 //    matrices, 1500 x 2048 4.1 -> 4.5 us); fixed-order
 //    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
-//    short fixed-order rows R = 1 in blocks of 256.
+//    fixed-order rows of 4 or 6 chunks in such matrices R = 2 in blocks of
+//    256 (2600 values 95.8 -> 87.2 us, 3072 78.9 -> 75.9), other short
+//    fixed-order rows R = 1 in blocks of 256.
 //  * Longer rows: the R that pads the last chain least -- 8, 5 or 4 for
 //    free order, 2 or 4 for fixed order (R = 2 only while a row stays within
 //    the flat kernel's 64 groups) -- the larger one on a tie, default blocks.
@@ -150,8 +152,8 @@ RowShape rows_auto_shape(uint64_t rows, uint64_t cols, int cu_count, const OpDef
     if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
     // (only with rows for four rounds of the R = 1 stream: smaller matrices
     // are latency-bound and want the wavefronts)
-    if (!fixed && chunks >= 4 && chunks % 2 == 0 && rows >= 4 * 16 * uint64_t(cu_count))
-      return {2, 512};
+    if (chunks >= 4 && chunks % 2 == 0 && rows >= 4 * 16 * uint64_t(cu_count))
+      return {2, fixed ? 256 : 512};
     return {1, fixed ? 256 : 512};
   }
   auto waste = [&](uint64_t r) { return ceil_div(chunks, r) * r - chunks; };
