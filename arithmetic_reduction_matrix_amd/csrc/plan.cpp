@@ -124,11 +124,12 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 //  * Rows of fewer than 8 chunks carry a fixed cost per row (the chain's
 //    result, the row combine, the store) that more wavefronts hide: R = 1
 //    (16 wavefronts per compute unit) in blocks of 512 threads, except free-
-//    order rows of 4 or 6 chunks in matrices of at least four rounds of that
-//    stream, which take R = 2 (half the chains per row, the same loads in
-//    flight; 2600-value rows 88.0 -> 83.1 us, 2048 79.1 -> 77.7, 3072
-//    78.9 -> 77.3; 2-chunk rows lose, 79.9 -> 97.6 us, and so do small
-//    matrices, 1500 x 2048 4.1 -> 4.5 us); fixed-order
+//    order rows of 4, 6 or 7 chunks in matrices of at least four rounds of
+//    that stream, which take R = 2 (half the chains per row, the same loads
+//    in flight; 2600-value rows 88.0 -> 83.1 us, 2048 79.1 -> 77.7, 3072
+//    78.9 -> 77.3, 3200 86.1 -> 81.4, 3584 79.2 -> 76.6; 2-chunk rows lose,
+//    79.9 -> 97.6 us, 5-chunk rows 80.8 -> 83.8, 3-chunk rows gain or lose
+//    by width, and small matrices lose, 1500 x 2048 4.1 -> 4.5 us); fixed-order
 //    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
 //    fixed-order rows of 4 or 6 chunks in such matrices R = 2 in blocks of
 //    256 (2600 values 95.8 -> 87.2 us, 3072 78.9 -> 75.9), other short
@@ -152,8 +153,8 @@ RowShape rows_auto_shape(uint64_t rows, uint64_t cols, int cu_count, const OpDef
     if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
     // (only with rows for four rounds of the R = 1 stream: smaller matrices
     // are latency-bound and want the wavefronts)
-    if (chunks >= 4 && chunks % 2 == 0 && rows >= 4 * 16 * uint64_t(cu_count))
-      return {2, fixed ? 256 : 512};
+    const bool pair = chunks == 4 || chunks == 6 || (!fixed && chunks == 7);
+    if (pair && rows >= 4 * 16 * uint64_t(cu_count)) return {2, fixed ? 256 : 512};
     return {1, fixed ? 256 : 512};
   }
   auto waste = [&](uint64_t r) { return ceil_div(chunks, r) * r - chunks; };

@@ -130,9 +130,9 @@ typedef struct armx_config {
  * of whole 128-byte lines -- which armx_launch_plan reports as chain_r;
  * chain_r has no effect there; rows of more than 32 values use up to 64 KiB
  * of LDS per block to hold a chunk of row sums); rows of 513 to 3584 values take R = 1
- * and blocks of 512 threads (rows of 4 or 6 chunks of 512 when there are at
- * least 64 rows per compute unit: R = 2, fixed order in blocks of 256, unless
- * a fixed-order row is exactly 4 chunks; fixed order: R = 2 or 4 and 512 threads when a
+ * and blocks of 512 threads (rows of 4 or 6 chunks of 512, free-order rows of
+ * 7, when there are at least 64 rows per compute unit: R = 2, fixed order in
+ * blocks of 256, unless a fixed-order row is exactly 4 chunks; fixed order: R = 2 or 4 and 512 threads when a
  * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
  * rows the R that leaves a row's last chain of R chunks the least padding,
  * 8, 5 or 4 (fixed order: 2 or 4), with the default block size.  An explicit
