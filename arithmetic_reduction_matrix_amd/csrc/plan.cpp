@@ -120,7 +120,7 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 // MI355X with 2^28 values.  A row stream keeps two chains in flight per
 // wavefront whatever they hold, so a row's last chain should be as full as
 // possible: one that holds a single chunk costs about as long as a full one
-// (9-chunk rows at R = 8: 172 us against 77 us at R = 3).
+// (9-chunk rows at R = 8: 111 us against 77 us at R = 5).
 //  * Rows of fewer than 8 chunks carry a fixed cost per row (the chain's
 //    result, the row combine, the store) that more wavefronts hide: R = 1
 //    (16 wavefronts per compute unit) in blocks of 512 threads, except free-
@@ -134,13 +134,27 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 //    fixed-order rows of 4 or 6 chunks in such matrices R = 2 in blocks of
 //    256 (2600 values 95.8 -> 87.2 us, 3072 78.9 -> 75.9), other short
 //    fixed-order rows R = 1 in blocks of 256.
-//  * Longer rows: the R that pads the last chain least -- 8, 5 or 4 for
-//    free order, 2 or 4 for fixed order (R = 2 only while a row stays within
-//    the flat kernel's 64 groups) -- the larger one on a tie, default blocks.
-//    Free order skips R = 6 and 7: their grids hold 3 wavefronts per compute
-//    unit, which streamed rows measurably worse (768 rows of 348712 values:
-//    97.4 us at R = 6 against 78.7 us at R = 4; over 24 row counts at 2^28
-//    values the slowest shape went from 1.24 to 1.08 times its best R).
+//  * Longer fixed-order rows: the R of 2 and 4 that pads the last group
+//    least (R = 2 only while a row stays within the flat kernel's 64
+//    groups), 4 on a tie, default blocks.
+//  * Longer free-order rows, default blocks.  8 to 13 chunks: the R of 8, 5
+//    and 4 that pads the last chain least, the larger on a tie, except that
+//    rows of 8 chunks ending inside the last one take R = 4 (such a row is
+//    one masked chain at R = 8, two wavefronts per compute unit, and streams
+//    slower than a whole one: 3992 values 87.9 us at R = 8, 77.6 at R = 4,
+//    where 4096 values run 74.2 us at R = 8).  14 chunks or more: R = 8
+//    when the padding of its last chain is at most a fifth of the row and,
+//    below 22 chunks (at most three chains of 8), at most one chunk; else
+//    R = 4.  Measured over 23 lengths from 14 to 64 chunks this is within
+//    about 1 us of the better of R = 4 and 8 (22 chunks 76.7 us at R = 8
+//    against 77.6 at R = 4, 20 chunks 79.9 against 77.3, 25 chunks 80.5
+//    against 77.3, 50 chunks 77.3 against 80.5); R = 5 pads less in some of
+//    these and is never measurably faster than that better one (20 chunks
+//    78.2 us, 25 chunks 78.8).  Free order skips R = 6
+//    and 7: their grids hold 3 wavefronts per compute unit, which streamed
+//    rows measurably worse (768 rows of 348712 values: 97.4 us at R = 6
+//    against 78.7 us at R = 4; over 24 row counts at 2^28 values the slowest
+//    shape went from 1.24 to 1.08 times its best R).
 struct RowShape {
   uint64_t r;
   int block;
@@ -162,6 +176,12 @@ RowShape rows_auto_shape(uint64_t rows, uint64_t cols, int cu_count, const OpDef
     const uint64_t r = (waste(2) < waste(4) && ceil_div(chunks, 2) <= 64) ? 2 : 4;
     return {r, d.block};
   }
+  if (chunks >= 14) {
+    const uint64_t w8 = waste(8);
+    const bool r8 = 5 * w8 <= chunks && (chunks >= 22 || w8 <= 1);
+    return {r8 ? uint64_t(8) : uint64_t(4), d.block};
+  }
+  if (chunks == 8 && cols % kChunk != 0) return {4, d.block};
   uint64_t best = 8;
   for (uint64_t r : {uint64_t(5), uint64_t(4)})
     if (waste(r) < waste(best)) best = r;

@@ -41,6 +41,7 @@
 // the row's own chunks is -0.0, and adding +0.0 to such a node leaves it as it
 // is, exactly as -0.0 would.
 #include "fixed_tree.hpp"
+#include "row_tail.hpp"
 #include "launch.h"
 
 namespace armx {
@@ -61,7 +62,9 @@ __device__ __forceinline__ float group_root(const u32x4 (&v)[R]) {
   }
 }
 
-template <int R, bool NT, bool MMA>
+// PARTIAL: whether rows end inside a group (instantiated apart, so that whole
+// groups carry no masking code at all).
+template <int R, bool NT, bool MMA, bool PARTIAL>
 __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                                 uint64_t cols, uint64_t ld,
                                                 float* __restrict__ out, uint64_t g, uint64_t T,
@@ -69,9 +72,10 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   if (g >= rows) return;
   const uint64_t group_elems = uint64_t(R) * 512;
   const uint64_t gpr = (cols + group_elems - 1) / group_elems;
-  const bool partial = gpr * group_elems != cols;
   const uint64_t last_chunk = (cols - 1) / 512;
   const u32x4* fill = neg_zero_chunk();
+  u32x4 keep[R];
+  if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * gpr;
   const uint64_t row_step = T * ld;
@@ -89,7 +93,9 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   };
   float slots = -0.0f;
   auto reduce = [&](u32x4 (&v)[R]) {
-    if (partial && rc + 1 == gpr) mask_row_chain<R>(v, rc, cols, 0x8000u, lane);
+    if constexpr (PARTIAL) {
+      if (rc + 1 == gpr) apply_row_tail<R>(v, keep, 0x8000u);
+    }
     const float node = group_root<R, MMA>(v);
     slots = uint64_t(lane) == rc ? node : (rc == 0 ? -0.0f : slots);
     const float root = lane_tree_full(slots);
@@ -171,7 +177,11 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
       const uint64_t T = uint64_t(gridDim.x) * W;
       // the last row stays out of the stream when rows end inside a group
       const bool tail = cols % (uint64_t(R) * 512) != 0;
-      rows_fixed_flat<R, NT, MMA>(x, tail ? rows - 1 : rows, cols, ld, out, g, T, lane);
+      if (tail) {
+        rows_fixed_flat<R, NT, MMA, true>(x, rows - 1, cols, ld, out, g, T, lane);
+      } else {
+        rows_fixed_flat<R, NT, MMA, false>(x, rows, cols, ld, out, g, T, lane);
+      }
       if (tail && g == (rows - 1) % T) {
         const float root = row_root_masked<R, NT, MMA>(x + (rows - 1) * ld, cols, lane);
         if (lane == 0) out[rows - 1] = root;

@@ -26,6 +26,7 @@
 //  * otherwise each block sums a row (looping over rows if needed) and its W
 //    wavefronts take the row's chains round-robin, combined through LDS.
 #include "device_common.hpp"
+#include "row_tail.hpp"
 #include "launch.h"
 
 namespace armx {
@@ -50,18 +51,22 @@ struct RowCursor {
 // a chain): loads run ahead across row boundaries, so the pipeline never
 // drains between rows.  A row that is not a whole number of chains ends in a
 // partial chain, read and masked as load_row_chain and mask_row_chain
-// describe (values past the row count as +0.0).  At the end of a row its
-// total is written and the running sum restarts.
-template <int R, bool NT, int D>
+// describe (values past the row count as +0.0; the masks are computed once,
+// by row_tail_keep).  At the end of a row its total is written and the
+// running sum restarts.
+// PARTIAL: whether rows end inside a chain (instantiated apart, so that whole
+// chains carry no masking code at all).
+template <int R, bool NT, int D, bool PARTIAL>
 __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                           uint64_t cols, uint64_t ld, float* __restrict__ out,
                                           uint64_t g, uint64_t T, int lane) {
   if (g >= rows) return;
   const uint64_t chain_elems = uint64_t(R) * 512;
   const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
-  const bool partial = cpr * chain_elems != cols;
   const uint64_t last_chunk = (cols - 1) / 512;
   const u32x4* fill = neg_zero_chunk();
+  u32x4 keep[R];
+  if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
   const uint64_t K = (rows - 1 - g) / T + 1;
   const uint64_t items = K * cpr;
   const uint64_t row_step = T * ld;
@@ -95,7 +100,9 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
   };
   auto reduce = [&](u32x4 (&v)[R]) {
     retire();
-    if (partial && rd.c + 1 == cpr) mask_row_chain<R>(v, rd.c, cols, 0u, lane);
+    if constexpr (PARTIAL) {
+      if (rd.c + 1 == cpr) apply_row_tail<R>(v, keep, 0u);
+    }
     pending = chain_value<R, D>(v);
     have_pending = true;
     rd.next(cpr);
@@ -141,7 +148,11 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
     const uint64_t T = uint64_t(gridDim.x) * W;
     // the last row stays out of the stream when rows end inside a chain
     const uint64_t streamed = tail ? rows - 1 : rows;
-    rows_flat<R, NT, D>(x, streamed, cols, ld, out, g, T, lane);
+    if (tail) {
+      rows_flat<R, NT, D, true>(x, streamed, cols, ld, out, g, T, lane);
+    } else {
+      rows_flat<R, NT, D, false>(x, streamed, cols, ld, out, g, T, lane);
+    }
     if (tail && g == (rows - 1) % T) {
       const float total = row_total_masked<R, NT, D>(x + (rows - 1) * ld, cols, lane);
       if (lane == 0) out[rows - 1] = total;

@@ -56,7 +56,11 @@ int main(int argc, char** argv) {
         {ARMX_OP_ROWS_FIXED, 65536, 4096, 4096, 1, 0, 1, 4, 0},
         {ARMX_OP_ROWS, 4096, 65536, 65536, 1, 0, 1, 8, 0},
         {ARMX_OP_ROWS, 57344, 4608, 4608, 1, 0, 1, 5, 0},        // 9 chunks: 5 + 4
-        {ARMX_OP_ROWS, 16384, 16896, 16896, 1, 0, 1, 5, 0},      // 33 chunks: waste 2, no R 7
+        {ARMX_OP_ROWS, 16384, 16896, 16896, 1, 0, 1, 4, 0},      // 33 chunks: 8 would pad 7
+        {ARMX_OP_ROWS, 67243, 3992, 3992, 1, 0, 1, 4, 1},        // 8 chunks ending inside one
+        {ARMX_OP_ROWS, 26483, 10136, 10136, 1, 0, 1, 4, 1},      // 20 chunks: 3 chains of 8
+        {ARMX_OP_ROWS, 24053, 11160, 11160, 1, 0, 1, 8, 1},      // 22 chunks: 8 pads 2
+        {ARMX_OP_ROWS, 10528, 25496, 25496, 1, 0, 1, 8, 1},      // 50 chunks: 8 pads 6
         {ARMX_OP_ROWS, 4096, 65024, 65024, 1, 0, 1, 8, 0},       // 127 chunks: waste 1
         {ARMX_OP_ROWS_FIXED, 57344, 4608, 4608, 1, 0, 1, 2, 0},  // 9 chunks
         {ARMX_OP_ROWS_FIXED, 37449, 7168, 7168, 1, 0, 1, 2, 0},  // 14 chunks
