@@ -134,8 +134,12 @@ typedef struct armx_config {
  * 7, when there are at least 64 rows per compute unit: R = 2, fixed order in
  * blocks of 256, unless a fixed-order row is exactly 4 chunks; fixed order: R = 2 or 4 and 512 threads when a
  * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
- * rows the R that leaves a row's last chain of R chunks the least padding,
- * 8, 5 or 4 (fixed order: 2 or 4), with the default block size.  An explicit
+ * rows, with the default block size: fixed order the R of 2 and 4 that
+ * leaves a row's last group of R chunks the least padding; free order, rows
+ * of 8 to 13 chunks the R of 8, 5 and 4 that pads the last chain least (rows
+ * of 8 chunks that end inside the last: R = 4), rows of 14 chunks or more
+ * R = 8 when that pads the last chain by at most a fifth of the row (below
+ * 22 chunks: by at most one chunk), else R = 4.  An explicit
  * block_threads or chain_r overrides its part, except that rows of at most
  * 512 values with ARMX_FLAG_MMA_LEAVES run blocks of at most 256 threads (a
  * larger block_threads is lowered; no row's result depends on it). */
