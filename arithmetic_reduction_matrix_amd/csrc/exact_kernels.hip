@@ -36,6 +36,8 @@
 // (+Inf, -Inf or NaN) instead of adding to the integers; the result follows
 // IEEE addition (NaN if any NaN or both infinities, else the infinity), and
 // the 128-bit output is then 0.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.h"
 
@@ -228,14 +230,63 @@ __device__ __forceinline__ void stream_exact(const u32x4* __restrict__ x, uint64
   if (iters & 1) add(p);  // p holds the last chain
 }
 
+// One 32-bit word of lane (lane within its row rotated right by CTRL's amount).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_word(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return uint64_t(dpp_word<CTRL>(uint32_t(v >> 32))) << 32 | dpp_word<CTRL>(uint32_t(v));
+}
+
+// a + (a of another lane), the other lane's words given as they arrived.
+__device__ __forceinline__ void add_words(Exact& a, uint32_t hh, uint32_t hl, uint32_t lh,
+                                          uint32_t ll, uint32_t f) {
+  a.hi += int64_t(uint64_t(hh) << 32 | hl);
+  a.lo += uint64_t(lh) << 32 | ll;
+  a.flags |= f;
+}
+
+// The two halves of a lane-pair exchange (v_permlane16_swap or
+// v_permlane32_swap with both operands the same register): p[0] + p[1] pairs
+// every lane with lane ^ 16 (or ^ 32) for any commutative operation.
+template <bool X32>
+__device__ __forceinline__ Exact add_swapped(const Exact& a) {
+  auto sw = [](uint32_t v) {
+    if constexpr (X32) {
+      return __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    } else {
+      return __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    }
+  };
+  const auto hh = sw(uint32_t(uint64_t(a.hi) >> 32)), hl = sw(uint32_t(uint64_t(a.hi)));
+  const auto lh = sw(uint32_t(a.lo >> 32)), ll = sw(uint32_t(a.lo));
+  const auto f = sw(a.flags);
+  Exact r{int64_t(uint64_t(hh[0]) << 32 | hl[0]), uint64_t(lh[0]) << 32 | ll[0], f[0]};
+  add_words(r, hh[1], hl[1], lh[1], ll[1], f[1]);
+  return r;
+}
+
 // Sum over the 64 lanes (every lane gets it); any order, the sums are exact.
+// Row rotations (DPP) within each 16-lane row, then the row pairs and halves
+// exchanged with the permlane swaps: no LDS round trips.
 __device__ __forceinline__ Exact wave_exact(Exact a) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    a.hi += int64_t(__shfl_xor((long long)a.hi, m));
-    a.lo += uint64_t(__shfl_xor((unsigned long long)a.lo, m));
-    a.flags |= unsigned(__shfl_xor(int(a.flags), m));
-  }
+  auto rot = [&](auto ctl) {
+    constexpr int C = decltype(ctl)::value;
+    const uint64_t h = dpp_u64<C>(uint64_t(a.hi)), l = dpp_u64<C>(a.lo);
+    const uint32_t f = dpp_word<C>(a.flags);
+    a.hi += int64_t(h);
+    a.lo += l;
+    a.flags |= f;
+  };
+  rot(std::integral_constant<int, kDppRor8>{});
+  rot(std::integral_constant<int, kDppRor4>{});
+  rot(std::integral_constant<int, kDppRor2>{});
+  rot(std::integral_constant<int, kDppRor1>{});
+  a = add_swapped<false>(a);
+  a = add_swapped<true>(a);
   fold(a);
   return a;
 }
@@ -360,6 +411,9 @@ __global__ __launch_bounds__(LIMBS ? kExactLimbsMaxBlock : 1024) void exact_kern
   LimbSums ls{{0, 0, 0, 0}, 0, 0};
   const uint64_t c0 = c;
   const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
+  // No request pacing (pace_pause): the binary64 additions already space a
+  // wavefront's requests, and a pause on top lost (2^28: 76.0 -> 88.7 us at
+  // the free-order sum's pauses).
   stream_exact<R, NT, LIMBS>(x, c, iters, total_waves, lane, a, ls);
   c += iters * total_waves;
   // the partial chain at the end: values past n read as +0.0
