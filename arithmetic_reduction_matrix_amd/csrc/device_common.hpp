@@ -389,76 +389,6 @@ __device__ __forceinline__ void tail_chain(const uint16_t* __restrict__ xh, uint
   chain_step<R, D>(v, run);
 }
 
-// ---- rows that end inside a chain --------------------------------------------
-//
-// A row-major matrix of `rows` rows of `cols` values (cols > 512) with pitch
-// ld >= cols, a multiple of 8 when there is more than one row, so every row
-// starts 16-byte aligned.  The chunk grid restarts at every row, and a row's
-// last chain of R chunks may end inside the row's last chunk or before it.
-// In such a chain, chunks past the row's last chunk are read from
-// kNegZeroChunk, 1 KiB of -0.0 that stays in the caches (rereading the row's
-// own last chunk instead costs HBM traffic: non-temporal loads do not keep
-// it); -0.0 adds nothing in either order.  In the last chunk the lanes past
-// the row read on into the pitch and the next row: at most 511 values past
-// the row, so inside the matrix for every row but the last (the next row
-// starts at most ld values on and holds more than 512).  The pipelined
-// streams therefore leave the last row of the matrix to a path with exact
-// masked loads, and the values of the last chunk that are not the row's are
-// replaced by `fill` in registers.
-struct NegZeroChunk {
-  uint32_t w[256];
-  constexpr NegZeroChunk() : w() {
-    for (int i = 0; i < 256; ++i) w[i] = 0x80008000u;
-  }
-};
-// Never written.  Not const, and with external (inline) linkage, so that the
-// optimiser cannot fold its contents into the loads that may read it: it
-// would turn them into selects and branches, and the loop would no longer
-// keep every load unconditional.
-__device__ inline NegZeroChunk kNegZeroChunk{};
-
-__device__ __forceinline__ const u32x4* neg_zero_chunk() {
-  return reinterpret_cast<const u32x4*>(kNegZeroChunk.w);
-}
-
-// Loads chain c of the row at xr (R chunks, 16 bytes per lane each); chunks
-// past `last_chunk` are read from `fill` (neg_zero_chunk()).
-template <int R, bool NT>
-__device__ __forceinline__ void load_row_chain(const uint16_t* __restrict__ xr, uint64_t c,
-                                               uint64_t last_chunk, const u32x4* fill, int lane,
-                                               u32x4 (&v)[R]) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint64_t ci = c * R + uint64_t(r);
-    const u32x4* p = ci <= last_chunk ? reinterpret_cast<const u32x4*>(xr) + ci * 64 : fill;
-    v[r] = load16<NT>(p + lane);
-  }
-}
-
-// Replaces the values of chain c (as loaded by load_row_chain) at or past
-// cols by `fill` (a binary16 pattern; chunks wholly past cols already hold
-// -0.0, and are left as they are when fill is -0.0).  Straight-line code
-// (selects only): a branch here leaves the compiler unable to count the loads
-// still in flight, and it then waits for all of them, the prefetched next
-// chain included.
-template <int R>
-__device__ __forceinline__ void mask_row_chain(u32x4 (&v)[R], uint64_t c, uint64_t cols,
-                                               uint32_t fill, int lane) {
-  const uint32_t f2 = fill | (fill << 16);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint64_t cs = (c * R + uint64_t(r)) * 512;
-    const uint64_t in_chunk = cs >= cols ? 0 : (cols - cs > 512 ? 512 : cols - cs);
-    const int left = int(in_chunk) - lane * 8;   // values of this lane's slot in the row
-    const int k = left < 0 ? 0 : (left > 8 ? 8 : left);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t keep = (2 * w < k ? 0xFFFFu : 0u) | (2 * w + 1 < k ? 0xFFFF0000u : 0u);
-      v[r][w] = (v[r][w] & keep) | (f2 & ~keep);
-    }
-  }
-}
-
 // The wavefront total of the running per-lane sums (valid in every lane).
 template <int D>
 __device__ __forceinline__ float wave_total(float run) {

@@ -156,6 +156,13 @@ constexpr int kShortMmaMaxBlock = 256;
 // microseconds) only when a wavefront's share of a row without it is large:
 // at least kSplitMinShare values (64 KiB); no segment is made smaller than
 // kSplitMinSegment values.
+// Free-order row streams (one wavefront per row) of rows of at least
+// kRowsLongMinCols values, in blocks of at most kRowsStreamMaxBlock threads,
+// run as a kernel of their own, compiled for such blocks (more registers per
+// wavefront than a kernel that may run 1024-thread blocks).
+constexpr int kRowsStreamMaxBlock = 512;
+constexpr uint64_t kRowsLongMinCols = 32768;
+
 constexpr uint64_t kSplitMaxBlocks = 512;
 constexpr uint64_t kSplitMaxItems = 8192;
 static_assert(kSplitMaxItems == kSplitMaxBlocks * kMaxWaves, "a split grid's parts fit the stage");

@@ -14,8 +14,9 @@
 //    each wavefront owns rows g, g + T, ...; it streams (row, group) items
 //    with a software pipeline that runs across rows; a row's last group may
 //    end inside the row, and its values past the row are -0.0 (read and
-//    masked as load_row_chain and mask_row_chain describe; the matrix's last
-//    row then takes exact masked loads instead), so it is still the subtree
+//    masked as load_row_chain and mask_row_chain describe; the last group of
+//    the matrix's last row is read after the stream with load_last_chain,
+//    which reads nothing past the row), so it is still the subtree
 //    of its R-aligned chunks; a group's subtree root is selected
 //    into lane (group index) of a slot register, and the row root is
 //    lane_tree_full of that register (lanes past the row's groups hold -0.0,
@@ -77,19 +78,20 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   u32x4 keep[R];
   if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
   const uint64_t K = (rows - 1 - g) / T + 1;
-  const uint64_t items = K * gpr;
+  const bool last_apart = PARTIAL && g + (K - 1) * T == rows - 1;
+  const uint64_t items = K * gpr - (last_apart ? 1 : 0);   // streamed (row, group) items
   const uint64_t row_step = T * ld;
-  uint64_t lk = 0, lc = 0;   // next (row, group) to load
+  uint64_t lc = 0;           // group of the next item to load
   uint64_t rk = 0, rc = 0;   // next (row, group) to reduce
+  uint64_t issued = 0;
   const uint16_t* load_row = x + g * ld;
   auto load = [&](u32x4 (&v)[R]) {
-    load_row_chain<R, NT>(load_row, lc, last_chunk, fill, lane, v);
-    // stays on the last item once it is reached (the re-read is not used)
+    load_row_chain_counted<R, NT, PARTIAL>(load_row, lc, last_chunk, fill, lane, v);
+    // stays on the last streamed item once it is reached (the re-read is not used)
+    const bool more = ++issued < items;
     const bool more_in_row = lc + 1 < gpr;
-    const bool more_rows = lk + 1 < K;
-    lc = more_in_row ? lc + 1 : (more_rows ? 0 : lc);
-    lk = more_in_row ? lk : (more_rows ? lk + 1 : lk);
-    load_row = (!more_in_row && more_rows) ? load_row + row_step : load_row;
+    lc = more ? (more_in_row ? lc + 1 : 0) : lc;
+    load_row = (more && !more_in_row) ? load_row + row_step : load_row;
   };
   float slots = -0.0f;
   auto reduce = [&](u32x4 (&v)[R]) {
@@ -104,61 +106,33 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
     rc = row_done ? 0 : rc + 1;
     rk = row_done ? rk + 1 : rk;
   };
-  u32x4 a[R], b[R];
-  load(a);
-  uint64_t j = 0;
-  for (; j + 1 < items; j += 2) {
-    load(b);
-    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
-    reduce(a);
-    load(a);
-    __builtin_amdgcn_sched_barrier(0);
-    reduce(b);
+  // The last group of the matrix's last row: its loads go out first, with
+  // the stream's first loads, and it is reduced after the stream.
+  u32x4 fin[R];
+  uint32_t fin_h[8];
+  if constexpr (PARTIAL) {
+    if (last_apart) load_last_chain<R, NT>(x + (rows - 1) * ld, gpr - 1, cols, lane, fin, fin_h);
   }
-  if (j < items) reduce(a);
-}
-
-// The root of one row of at most 64 groups, by one wavefront with no read
-// past the row: the same group subtrees and slot register as rows_fixed_flat,
-// its whole groups streamed with the same ping-pong pipeline, the partial last
-// group read with exact masked loads.
-template <int R, bool NT, bool MMA>
-__device__ __forceinline__ float row_root_masked(const uint16_t* __restrict__ xr, uint64_t cols,
-                                                 int lane) {
-  const uint64_t group_elems = uint64_t(R) * 512;
-  const uint64_t gpr = (cols + group_elems - 1) / group_elems;
-  const uint64_t gfull = cols / group_elems;
-  const u32x4* x4 = reinterpret_cast<const u32x4*>(xr);
-  float slots = -0.0f;
-  auto take = [&](uint64_t gi, const u32x4 (&v)[R]) {
-    const float node = group_root<R, MMA>(v);
-    slots = uint64_t(lane) == gi ? node : slots;
-  };
-  uint64_t gi = 0;
-  if (gfull > 0) {
+  if (items > 0) {
     u32x4 a[R], b[R];
-    load_group<R, NT>(x4, 0, lane, a);
-    for (; gi + 1 < gfull; gi += 2) {
-      load_group<R, NT>(x4, (gi + 1) * R, lane, b);
+    load(a);
+    uint64_t j = 0;
+    for (; j + 1 < items; j += 2) {
+      load(b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the reduction
+      reduce(a);
+      load(a);
       __builtin_amdgcn_sched_barrier(0);
-      take(gi, a);
-      load_group<R, NT>(x4, (gi + 2 < gfull ? gi + 2 : gi + 1) * R, lane, a);
-      __builtin_amdgcn_sched_barrier(0);
-      take(gi + 1, b);
+      reduce(b);
     }
-    if (gi < gfull) {
-      take(gi, a);
-      ++gi;
+    if (j < items) reduce(a);
+  }
+  if constexpr (PARTIAL) {
+    if (last_apart) {   // reduce() masks it and writes the row's root
+      merge_last_chain<R>(fin, fin_h, gpr - 1, cols, lane);
+      reduce(fin);
     }
   }
-  if (gi < gpr) {
-    u32x4 v[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      v[r] = load8_masked(xr, (gi * R + uint64_t(r)) * 512 + uint64_t(lane) * 8, cols, 0x8000u);
-    take(gi, v);
-  }
-  return lane_tree_full(slots);
 }
 
 template <int R, bool NT, bool MMA>
@@ -175,16 +149,10 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
     if constexpr (is_pow2(R)) {
       const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + wave_id();
       const uint64_t T = uint64_t(gridDim.x) * W;
-      // the last row stays out of the stream when rows end inside a group
-      const bool tail = cols % (uint64_t(R) * 512) != 0;
-      if (tail) {
-        rows_fixed_flat<R, NT, MMA, true>(x, rows - 1, cols, ld, out, g, T, lane);
+      if (cols % (uint64_t(R) * 512) != 0) {
+        rows_fixed_flat<R, NT, MMA, true>(x, rows, cols, ld, out, g, T, lane);
       } else {
         rows_fixed_flat<R, NT, MMA, false>(x, rows, cols, ld, out, g, T, lane);
-      }
-      if (tail && g == (rows - 1) % T) {
-        const float root = row_root_masked<R, NT, MMA>(x + (rows - 1) * ld, cols, lane);
-        if (lane == 0) out[rows - 1] = root;
       }
     }
     return;

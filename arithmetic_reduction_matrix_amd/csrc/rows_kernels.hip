@@ -16,7 +16,9 @@
 //    current row is finished, so the pipeline runs across rows, and a row's
 //    last partial chain is masked in registers (the matrix's last row then
 //    takes exact masked loads instead); no block synchronisation at all.
-//    Used when there are many rows.
+//    Used when there are many rows; rows of at least kRowsLongMinCols values
+//    run rows_stream_kernel, which keeps the last row in the stream and reads
+//    only its last chain apart.
 //  * rows_split_kernel (few rows, or a row stream whose last round would be
 //    poorly filled; with a workspace): every row is split over S wavefronts
 //    of several blocks, which take the row's chains round-robin as the flat
@@ -130,6 +132,119 @@ __device__ __forceinline__ float row_total_masked(const uint16_t* __restrict__ x
   stream_chains<R, NT, D>(reinterpret_cast<const u32x4*>(xr), 0, chains_full, 1, lane, run);
   if (chains_full * R * 512 < cols) tail_chain<R, D>(xr, chains_full, cols, lane, run);
   return wave_total<D>(run);
+}
+
+// rows_flat for long rows: the same stream, but the matrix's last row stays
+// in it (the owner wavefront streams all of its rows), and only that row's
+// last chain, whose pipelined loads would read on past the matrix, is read
+// apart after the stream with load_last_chain (nothing past the row).  On
+// few long rows the last row summed apart by its owner finished well after
+// the others (1000 rows of 268288 values: 107 us against 85 us streamed);
+// on rows under 64 chunks this form measured up to 3 us slower than
+// rows_flat (67243 rows of 3992 values: 80.5 against 77.3 us), so the
+// launch takes it from 32768 values per row on.
+template <int R, bool NT, int D, bool PARTIAL>
+__device__ __forceinline__ void rows_flat_long(const uint16_t* __restrict__ x, uint64_t rows,
+                                          uint64_t cols, uint64_t ld, float* __restrict__ out,
+                                          uint64_t g, uint64_t T, int lane) {
+  if (g >= rows) return;
+  const uint64_t chain_elems = uint64_t(R) * 512;
+  const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
+  const uint64_t last_chunk = (cols - 1) / 512;
+  const u32x4* fill = neg_zero_chunk();
+  u32x4 keep[R];
+  if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
+  const uint64_t K = (rows - 1 - g) / T + 1;
+  const bool last_apart = PARTIAL && g + (K - 1) * T == rows - 1;
+  // streamed (row, chain) items: fewer than 2^32 (the matrix holds at most
+  // 2^40 values, and every chain but a row's last holds 4096)
+  const uint32_t items = uint32_t(K * cpr - (last_apart ? 1 : 0));
+  const uint64_t row_step = T * ld;
+  RowCursor rd, pr;   // next item to reduce, to retire
+  uint64_t lc = 0;    // chain of the next item to load
+  uint32_t issued = 0;
+  const uint16_t* load_row = x + g * ld;
+  auto load = [&](u32x4 (&v)[R]) {
+    load_row_chain_counted<R, NT, PARTIAL>(load_row, lc, last_chunk, fill, lane, v);
+    // stays on the last streamed item once it is reached (the re-read is not used)
+    if (++issued < items) {
+      if (lc + 1 < cpr) {
+        ++lc;
+      } else {
+        lc = 0;
+        load_row += row_step;
+      }
+    }
+  };
+  // A chain's value joins the running sum one half-step later (after the next
+  // loads are issued), so waiting for it never delays a prefetch.
+  float run = 0.0f, pending = 0.0f;
+  bool have_pending = false;
+  auto retire = [&]() {
+    if (!have_pending) return;
+    run += pending;
+    have_pending = false;
+    if (pr.c + 1 == cpr) {
+      const float total = wave_total<D>(run);
+      if (lane == 0) out[g + pr.k * T] = total;
+      run = 0.0f;
+    }
+    pr.next(cpr);
+  };
+  auto reduce = [&](u32x4 (&v)[R]) {
+    retire();
+    if constexpr (PARTIAL) {
+      if (rd.c + 1 == cpr) apply_row_tail<R>(v, keep, 0u);
+    }
+    pending = chain_value<R, D>(v);
+    have_pending = true;
+    rd.next(cpr);
+  };
+  if (items > 0) {
+    u32x4 a[R], b[R];
+    load(a);
+    for (uint32_t j = 0; j < items; j += 2) {
+      load(b);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the tile steps
+      reduce(a);
+      load(a);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < items) reduce(b);
+    }
+    retire();
+  }
+  if constexpr (PARTIAL) {
+    if (last_apart) {
+      u32x4 fin[R];
+      uint32_t fin_h[8];
+      load_last_chain<R, NT>(x + (rows - 1) * ld, cpr - 1, cols, lane, fin, fin_h);
+      merge_last_chain<R>(fin, fin_h, cpr - 1, cols, lane);
+      apply_row_tail<R>(fin, keep, 0u);
+      run += chain_value<R, D>(fin);
+      const float total = wave_total<D>(run);
+      if (lane == 0) out[rows - 1] = total;
+    }
+  }
+}
+
+// The wave_rows mapping for rows of at least kRowsLongMinCols values, with
+// rows_flat_long, as a kernel of its own for blocks of at most
+// kRowsStreamMaxBlock threads (compiled for such blocks, a wavefront may hold
+// more than the 128 registers a 1024-thread block leaves, and at R = 8 it
+// needs them: rows_kernel spills there).
+template <int R, bool NT, int D>
+__global__ __launch_bounds__(kRowsStreamMaxBlock) void rows_stream_kernel(
+    const uint16_t* __restrict__ x, uint64_t rows, uint64_t cols, uint64_t ld,
+    float* __restrict__ out, int remap) {
+  const int lane = lane_id();
+  const uint64_t W = uint64_t(num_waves());
+  const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + uint64_t(wave_id());
+  const uint64_t T = uint64_t(gridDim.x) * W;
+  if (cols % (uint64_t(R) * 512) != 0) {
+    rows_flat_long<R, NT, D, true>(x, rows, cols, ld, out, g, T, lane);
+  } else {
+    rows_flat_long<R, NT, D, false>(x, rows, cols, ld, out, g, T, lane);
+  }
 }
 
 template <int R, bool NT, int D>
@@ -255,6 +370,13 @@ struct RowsK {
 };
 
 template <int R, bool NT, int D>
+struct StreamK {
+  static const void* ptr() {
+    return reinterpret_cast<const void*>(&rows_stream_kernel<R, NT, D>);
+  }
+};
+
+template <int R, bool NT, int D>
 struct SplitK {
   static const void* ptr() {
     return reinterpret_cast<const void*>(&rows_split_kernel<R, NT, D>);
@@ -280,13 +402,19 @@ hipError_t launch_rows(const Plan& plan, const void* x, float* out, void* ws,
     void* args[] = {&xh, &rows, &cols, &ld, &out, &segs, &w.counters, &w.partials};
     return launch_main(plan, fn, args, stream);
   }
-  const void* fn = kernel_for<RowsK>(plan.r, (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0,
-                                     chain_design(plan.flags));
-  if (!fn) return hipErrorInvalidValue;
+  const bool nt = (plan.flags & ARMX_FLAG_CACHED_LOADS) == 0;
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   uint64_t rows = plan.rows, cols = plan.n, ld = plan.ld;
   int wave_rows = plan.mode;
   int remap = plan.xcd_remap;
+  if (wave_rows && cols >= kRowsLongMinCols && plan.waves * 64 <= kRowsStreamMaxBlock) {
+    const void* fn = kernel_for<StreamK>(plan.r, nt, chain_design(plan.flags));
+    if (!fn) return hipErrorInvalidValue;
+    void* args[] = {&xh, &rows, &cols, &ld, &out, &remap};
+    return launch_main(plan, fn, args, stream);
+  }
+  const void* fn = kernel_for<RowsK>(plan.r, nt, chain_design(plan.flags));
+  if (!fn) return hipErrorInvalidValue;
   void* args[] = {&xh, &rows, &cols, &ld, &out, &wave_rows, &remap};
   return launch_main(plan, fn, args, stream);
 }

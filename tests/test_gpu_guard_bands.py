@@ -108,7 +108,8 @@ def test_short_rows_stay_in_bounds(rows, cols, cfg, fixed_order, mma_leaves):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (rows, cols, cfg)
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 700), (300, 4096), (4097, 2048 + 8)])
+@pytest.mark.parametrize("rows,cols", [(1, 1), (3, 700), (300, 4096), (4097, 2048 + 8),
+                                       (1000, 33001)])
 @pytest.mark.parametrize("fixed_order", [False, True])
 def test_row_entry_points_stay_in_bounds(rows, cols, fixed_order):
     ld = (cols + 7) // 8 * 8

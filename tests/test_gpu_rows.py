@@ -106,3 +106,24 @@ def test_full_4096x65536_normal():
     for cfg in (dict(), dict(plain=True)):
         got = armx.reduce_rows(xd, **cfg).cpu().numpy()
         check_rows(x, got, str(cfg))
+
+
+@pytest.mark.parametrize("cols", [33001, 36000, 40960])
+def test_long_rows_stream(cols):
+    # rows of at least 32768 values in a well-filled row stream take
+    # rows_stream_kernel: the matrix's last row stays in the stream and only
+    # its last chain is read apart (33001: the row ends inside a lane's 8
+    # values; 36000: inside a chain; 40960: whole chains of 8)
+    rows = 1000
+    ld = (cols + 7) // 8 * 8
+    x = si.generate_rows("normal", rows, cols, seed=cols)
+    pad = np.zeros((rows, ld), np.float16)
+    pad[:, :cols] = x
+    xd = to_dev(pad)[:, :cols]
+    # (a small grid keeps every chain length on the row stream)
+    small = [dict(chain_r=r, block_threads=64, grid_blocks=16) for r in (1, 2, 4, 5, 8)]
+    for cfg in [dict(), dict(plain=True), dict(all_ones=True),
+                dict(chain_r=3, block_threads=256, grid_blocks=8)] + small:
+        got = armx.reduce_rows(xd, **cfg).cpu().numpy()
+        check_rows(x, got, f"{rows}x{cols} {cfg}")
+

@@ -56,6 +56,23 @@ def test_block_chain_matrix(block, r):
     check(si.generate_rows("bits_finite", 24, 40_000, seed=r), block_threads=block, chain_r=r)
 
 
+@pytest.mark.parametrize("cols", [4001, 6000, 9000])
+@pytest.mark.parametrize("mma_leaves", [False, True])
+def test_row_stream_last_group(cols, mma_leaves):
+    # the flat row stream keeps the matrix's last row in it and reads only
+    # that row's last group apart (4001: the row ends inside a lane's 8
+    # values); a small grid puts every R on the stream
+    x = si.generate_rows("normal", 1500, cols, seed=cols)
+    extra = dict(mma_leaves=True) if mma_leaves else {}
+    for cfg in [dict()] + [dict(chain_r=r, block_threads=64, grid_blocks=16) for r in (1, 2, 4, 8)]:
+        if mma_leaves:
+            from oracle import fixed_tree_row_sums_mma_leaves
+            got = armx.reduce_rows_fixed_order(padded(x), **cfg, **extra).cpu().numpy()
+            assert np.array_equal(bits(got), bits(fixed_tree_row_sums_mma_leaves(x))), (cols, cfg)
+        else:
+            check(x, **cfg)
+
+
 def test_batch_invariance():
     x = si.generate_rows("logu_signed", 512, 8192, seed=17)
     want = bits(fixed_tree_row_sums(x))
