@@ -414,8 +414,14 @@ int make_plan(int op, uint64_t n_or_rows, uint64_t cols, uint64_t ld,
       grid = rows;
       const uint64_t cpr = ceil_div(cols, R * kChunk);   // chains per row
       if (allow_split && rows > 0 && 4 * rows * W < 3 * waves && cols / W >= kSplitMinShare) {
-        // the row's chains are dealt round-robin to its S wavefronts
-        uint64_t S = ceil_div(waves, rows);
+        // the row's chains are dealt round-robin to its S wavefronts; S
+        // rounds the grid's wavefront count per row down, so that the parts
+        // fit that count and the blocks cover the compute units (rounding up
+        // gave rows x S just over it, three wavefronts per block and blocks
+        // on two thirds of the units: 2^28 values, 20 rows 87.5 -> 79.8 us,
+        // 13 rows 86.5 -> 79.5, 3 rows 80.4 -> 77.1, 250 rows 85.9 -> 81.7;
+        // 200 rows 85.8 -> 86.2)
+        uint64_t S = waves / rows >= 2 ? waves / rows : ceil_div(waves, rows);
         S = S < cpr ? S : cpr;
         S = S < cols / kSplitMinSegment ? S : cols / kSplitMinSegment;
         S = S < kSplitMaxSegs ? S : kSplitMaxSegs;   // what the last block's tree holds
