@@ -324,13 +324,28 @@ __device__ __forceinline__ void store_record(uint64_t* rec, const Exact& a) {
 }
 
 // Sum of `count` published records; valid in wavefront 0.
+// (records loaded two per thread at a time, so that their loads are in
+// flight together; the sums are exact, so the order does not matter)
 __device__ Exact combine_records(const uint64_t* recs, unsigned count, ExactLds& s) {
   Exact a{0, 0, 0};
-  for (unsigned i = threadIdx.x; i < count; i += blockDim.x) {
-    const uint64_t* r = recs + uint64_t(i) * kRecordWords;
-    a.hi += int64_t(__hip_atomic_load(r + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    a.lo += __hip_atomic_load(r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.flags |= unsigned(__hip_atomic_load(r + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const unsigned B = blockDim.x;
+  for (unsigned i0 = threadIdx.x; i0 < count; i0 += 2 * B) {
+    uint64_t w[2][3];
+#pragma unroll
+    for (unsigned k = 0; k < 2; ++k) {
+      const unsigned i = i0 + k * B;
+      const uint64_t* r = recs + uint64_t(i) * kRecordWords;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        w[k][j] = i < count ? __hip_atomic_load(r + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0;
+    }
+#pragma unroll
+    for (unsigned k = 0; k < 2; ++k) {
+      a.hi += int64_t(w[k][0]);
+      a.lo += w[k][1];
+      a.flags |= unsigned(w[k][2]);
+    }
   }
   fold(a);
   return block_exact(wave_exact(a), s);

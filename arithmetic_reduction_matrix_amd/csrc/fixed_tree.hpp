@@ -169,9 +169,17 @@ __device__ inline float tree_of_values(const float* vals, unsigned count, float*
     float stk[kStack];
 #pragma unroll
     for (int j = 0; j < kStack; ++j) stk[j] = -0.0f;
-    for (unsigned k = 0; k < per; ++k) {
-      const unsigned i = t * per + k;
-      counter_push(stk, k, i < count ? load_published(vals + i) : -0.0f);
+    // the leaves are pushed in order; their loads go out four at a time
+    for (unsigned k0 = 0; k0 < per; k0 += 4) {
+      float leaf[4];
+#pragma unroll
+      for (unsigned j = 0; j < 4; ++j) {
+        const unsigned i = t * per + k0 + j;
+        leaf[j] = (k0 + j < per && i < count) ? load_published(vals + i) : -0.0f;
+      }
+#pragma unroll
+      for (unsigned j = 0; j < 4; ++j)
+        if (k0 + j < per) counter_push(stk, k0 + j, leaf[j]);
     }
     v = counter_fold(stk, per);
   }
