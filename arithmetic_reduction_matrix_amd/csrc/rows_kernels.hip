@@ -5,9 +5,9 @@
 // row goes through one v_mfma_f32_16x16x32_f16 against the signed ones
 // operand (or all ones with ARMX_FLAG_ALL_ONES; or, with ARMX_FLAG_PLAIN,
 // per-lane fp32 adds; the designs of device_common.hpp) and R of them chain
-// into the fp32 accumulators.  A chunk never straddles two rows: the chunk grid restarts
-// at every row (rows are 16-byte aligned because ld is a multiple of 8), and
-// a row's last partial chain is masked.  Rows of at most 512 values go to
+// into the fp32 accumulators.  A chunk never straddles two rows: the chunk
+// grid restarts at every row (rows are 16-byte aligned because ld is a
+// multiple of 8), and a row's last partial chain is masked.  Rows of at most 512 values go to
 // the segmented kernel of short_rows_kernels.hip instead.  The row's fp32
 // total is written directly, except in the split mapping, where a row's parts
 // meet in a workspace and the last block adds them.  The mappings:
@@ -145,8 +145,9 @@ __device__ __forceinline__ float row_total_masked(const uint16_t* __restrict__ x
 // launch takes it from 32768 values per row on.
 template <int R, bool NT, int D, bool PARTIAL>
 __device__ __forceinline__ void rows_flat_long(const uint16_t* __restrict__ x, uint64_t rows,
-                                          uint64_t cols, uint64_t ld, float* __restrict__ out,
-                                          uint64_t g, uint64_t T, int lane) {
+                                               uint64_t cols, uint64_t ld,
+                                               float* __restrict__ out, uint64_t g, uint64_t T,
+                                               int lane) {
   if (g >= rows) return;
   const uint64_t chain_elems = uint64_t(R) * 512;
   const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
