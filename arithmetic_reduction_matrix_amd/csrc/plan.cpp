@@ -128,12 +128,16 @@ void plan_short_rows(Plan& p, int cu_count, uint64_t W, int grid_cap) {
 //    that stream, which take R = 2 (half the chains per row, the same loads
 //    in flight; 2600-value rows 88.0 -> 83.1 us, 2048 79.1 -> 77.7, 3072
 //    78.9 -> 77.3, 3200 86.1 -> 81.4, 3584 79.2 -> 76.6; 2-chunk rows lose,
-//    79.9 -> 97.6 us, 5-chunk rows 80.8 -> 83.8, 3-chunk rows gain or lose
-//    by width, and small matrices lose, 1500 x 2048 4.1 -> 4.5 us); fixed-order
-//    rows of exactly 2 or 4 chunks are one group each (R = chunks), other
-//    fixed-order rows of 4 or 6 chunks in such matrices R = 2 in blocks of
-//    256 (2600 values 95.8 -> 87.2 us, 3072 78.9 -> 75.9), other short
-//    fixed-order rows R = 1 in blocks of 256.
+//    79.9 -> 97.6 us, 3-chunk rows gain or lose by width, and small matrices
+//    lose, 1500 x 2048 4.1 -> 4.5 us), and of 5 chunks, which take R = 3 in
+//    blocks of 64 (2456 values 82.3 -> 80.3 us, 2260 87.0 -> 84.6, 2560 78.2
+//    -> 77.4).  Fixed order: rows of exactly 2 or 4 chunks are one group each
+//    (R = chunks; 4 chunks in blocks of 256 in such matrices, 80.9 -> 74.8
+//    us), other rows of 2, 4 or 6 chunks in such matrices R = 2 in blocks of
+//    256 (2600 values 95.8 -> 87.2 us, 3072 78.9 -> 75.9, 920 89.7 -> 83.5,
+//    1000 82.0 -> 79.1), rows of 7 chunks R = 4 in blocks of 256 (3480
+//    values 85.5 -> 81.3 us, 3284 89.7 -> 85.3), other short rows R = 1 in
+//    blocks of 256.
 //  * Longer fixed-order rows: the R of 2 and 4 that pads the last group
 //    least (R = 2 only while a row stays within the flat kernel's 64
 //    groups), 4 on a tie, default blocks.
@@ -164,12 +168,19 @@ RowShape rows_auto_shape(uint64_t rows, uint64_t cols, int cu_count, const OpDef
                          bool fixed) {
   const uint64_t chunks = ceil_div(cols, kChunk);
   if (chunks < 8) {
-    if (fixed && (chunks == 2 || chunks == 4) && cols == chunks * kChunk) return {chunks, 512};
-    // (only with rows for four rounds of the R = 1 stream: smaller matrices
-    // are latency-bound and want the wavefronts)
-    const bool pair = chunks == 4 || chunks == 6 || (!fixed && chunks == 7);
-    if (pair && rows >= 4 * 16 * uint64_t(cu_count)) return {2, fixed ? 256 : 512};
-    return {1, fixed ? 256 : 512};
+    // (the other R only with rows for four rounds of the R = 1 stream:
+    // smaller matrices are latency-bound and want the wavefronts)
+    const bool many = rows >= 4 * 16 * uint64_t(cu_count);
+    if (fixed) {
+      if (chunks == 4 && cols == chunks * kChunk) return {4, many ? 256 : 512};
+      if (chunks == 2 && cols == chunks * kChunk) return {2, 512};
+      if (many && (chunks == 2 || chunks == 4 || chunks == 6)) return {2, 256};
+      if (many && chunks == 7) return {4, 256};
+      return {1, 256};
+    }
+    if (many && (chunks == 4 || chunks == 6 || chunks == 7)) return {2, 512};
+    if (many && chunks == 5) return {3, 64};
+    return {1, 512};
   }
   auto waste = [&](uint64_t r) { return ceil_div(chunks, r) * r - chunks; };
   if (fixed) {

@@ -129,11 +129,15 @@ typedef struct armx_config {
  * unit, 4 or 8 loads per step -- 4 for rows of more than 32 values at a pitch
  * of whole 128-byte lines -- which armx_launch_plan reports as chain_r;
  * chain_r has no effect there; rows of more than 32 values use up to 64 KiB
- * of LDS per block to hold a chunk of row sums); rows of 513 to 3584 values take R = 1
- * and blocks of 512 threads (rows of 4 or 6 chunks of 512, free-order rows of
- * 7, when there are at least 64 rows per compute unit: R = 2, fixed order in
- * blocks of 256, unless a fixed-order row is exactly 4 chunks; fixed order: R = 2 or 4 and 512 threads when a
- * row is exactly 2 or 4 chunks of 512, else R = 1 and 256 threads); longer
+ * of LDS per block to hold a chunk of row sums); rows of 513 to 3584 values
+ * (2 to 7 chunks of 512): free order R = 1 in blocks of 512 threads, and,
+ * when there are at least 64 rows per compute unit, R = 2 for rows of 4, 6
+ * or 7 chunks and R = 3 in blocks of 64 for rows of 5; fixed order R = 1 in
+ * blocks of 256, a row of exactly 2 or 4 chunks one group (R = 2 in blocks
+ * of 512, R = 4 in blocks of 512, or of 256 with at least 64 rows per
+ * compute unit), and with at least 64 rows per compute unit R = 2 in blocks
+ * of 256 for other rows of 2, 4 or 6 chunks and R = 4 in blocks of 256 for
+ * rows of 7; longer
  * rows, with the default block size: fixed order the R of 2 and 4 that
  * leaves a row's last group of R chunks the least padding; free order, rows
  * of 8 to 13 chunks the R of 8, 5 and 4 that pads the last chain least (rows

@@ -49,9 +49,11 @@ int main(int argc, char** argv) {
         {ARMX_OP_ROWS, 100000, 8, 8, 2, 0, 4, 8, 1},
         {ARMX_OP_ROWS, 100000, 512, 512, 2, 6, 4, 4, 0},
         {ARMX_OP_ROWS, 300000, 1000, 1000, 1, 0, 8, 1, 1},
-        {ARMX_OP_ROWS_FIXED, 300000, 1000, 1000, 1, 0, 4, 1, 1},
+        {ARMX_OP_ROWS_FIXED, 300000, 1000, 1000, 1, 0, 4, 2, 1},   // 2 chunks ending inside one
         {ARMX_OP_ROWS_FIXED, 300000, 1024, 1024, 1, 0, 8, 2, 0},
-        {ARMX_OP_ROWS_FIXED, 300000, 2048, 2048, 1, 0, 8, 4, 0},
+        {ARMX_OP_ROWS_FIXED, 300000, 2048, 2048, 1, 0, 4, 4, 0},   // one group, blocks of 256
+        {ARMX_OP_ROWS_FIXED, 77136, 3480, 3480, 1, 0, 4, 4, 1},    // 7 chunks
+        {ARMX_OP_ROWS, 109297, 2456, 2456, 1, 0, 1, 3, 1},         // 5 chunks
         {ARMX_OP_ROWS, 65536, 4096, 4096, 1, 0, 1, 8, 0},
         {ARMX_OP_ROWS_FIXED, 65536, 4096, 4096, 1, 0, 1, 4, 0},
         {ARMX_OP_ROWS, 4096, 65536, 65536, 1, 0, 1, 8, 0},
