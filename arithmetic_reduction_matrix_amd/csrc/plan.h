@@ -162,6 +162,9 @@ constexpr int kShortMmaMaxBlock = 256;
 // wavefront than a kernel that may run 1024-thread blocks).
 constexpr int kRowsStreamMaxBlock = 512;
 constexpr uint64_t kRowsLongMinCols = 32768;
+// Row streams read rows of fewer values than this through range-checked
+// buffer loads (32-bit byte offsets and record counts).
+constexpr uint64_t kRowsRangeMaxCols = uint64_t(1) << 29;
 
 constexpr uint64_t kSplitMaxBlocks = 512;
 constexpr uint64_t kSplitMaxItems = 8192;

@@ -14,16 +14,19 @@ namespace dev {
 // ld >= cols, a multiple of 8 when there is more than one row, so every row
 // starts 16-byte aligned.  The chunk grid restarts at every row, and a row's
 // last chain of R chunks may end inside the row's last chunk or before it.
-// In such a chain, chunks past the row's last chunk are read from
+// The row streams read such a chain with load_row_chain_range, which fetches
+// nothing past the row's last 16-byte lane slot.  In the plain form
+// (load_row_chain), chunks past the row's last chunk are read from
 // kNegZeroChunk, 1 KiB of -0.0 that stays in the caches (rereading the row's
 // own last chunk instead costs HBM traffic: non-temporal loads do not keep
-// it); -0.0 adds nothing in either order.  In the last chunk the lanes past
-// the row read on into the pitch and the next row: at most 511 values past
-// the row, so inside the matrix for every row but the last (the next row
-// starts at most ld values on and holds more than 512).  The pipelined
-// streams therefore read the last chain of the matrix's last row apart, with
-// load_last_chain, and the values of a last chain that are not the row's
-// are replaced by `fill` in registers.
+// it); -0.0 adds nothing in either order; and in the last chunk the lanes
+// past the row read on into the pitch and the next row: at most 511 values
+// past the row, so inside the matrix for every row but the last (the next
+// row starts at most ld values on and holds more than 512).  The range-checked
+// form reads the partly filled slot whole, inside the pitch, so it too may
+// not read the matrix's last row: the pipelined streams read the last chain
+// of that row apart, with load_last_chain, and the values of a last chain
+// that are not the row's are replaced by `fill` in registers.
 struct NegZeroChunk {
   uint32_t w[256];
   constexpr NegZeroChunk() : w() {
@@ -52,6 +55,28 @@ __device__ __forceinline__ void load_row_chain(const uint16_t* __restrict__ xr, 
     const u32x4* p = ci <= last_chunk ? reinterpret_cast<const u32x4*>(xr) + ci * 64 : fill;
     v[r] = load16<NT>(p + lane);
   }
+}
+
+// load_row_chain through a range-checked buffer descriptor over the row's
+// first `row_bytes` bytes (its cols values rounded up to whole 16-byte lane
+// slots): a lane whose slot starts at or past that end reads zeros without
+// any memory access, so the lanes past the row in its last chunk, and chunks
+// wholly past it, cost no fetch (with plain loads they read on into the next
+// row, which a non-temporal stream then fetches from HBM a second time).
+// Offsets are 32-bit: rows of less than 4 GiB.  The values past cols are
+// replaced by the masks of row_tail_keep as before.
+constexpr int kBufferWord3 = 0x00020000;   // raw buffer: 32-bit data, range-checked
+template <int R, bool NT>
+__device__ __forceinline__ void load_row_chain_range(const uint16_t* __restrict__ xr,
+                                                     uint32_t row_bytes, uint64_t c, int lane,
+                                                     u32x4 (&v)[R]) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xr), 0, int(row_bytes), kBufferWord3);
+  const uint32_t off = uint32_t(c) * uint32_t(R) * 1024u + uint32_t(lane) * 16u;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    v[r] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + uint32_t(r) * 1024u, 0, NT ? 2 : 0));
 }
 
 // load_row_chain with the chain's chunks inside the row counted once per

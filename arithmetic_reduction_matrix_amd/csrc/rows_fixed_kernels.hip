@@ -64,8 +64,11 @@ __device__ __forceinline__ float group_root(const u32x4 (&v)[R]) {
 }
 
 // PARTIAL: whether rows end inside a group (instantiated apart, so that whole
-// groups carry no masking code at all).
-template <int R, bool NT, bool MMA, bool PARTIAL>
+// groups carry no masking code at all).  RANGE (with PARTIAL, for rows of
+// less than 2 GiB): the groups are read by load_row_chain_range, so nothing
+// past a row's last 16-byte slot is fetched; the zeros it returns past the
+// row are masked to -0.0 like the rest of the last group.
+template <int R, bool NT, bool MMA, bool PARTIAL, bool RANGE = false>
 __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                                 uint64_t cols, uint64_t ld,
                                                 float* __restrict__ out, uint64_t g, uint64_t T,
@@ -75,6 +78,7 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   const uint64_t gpr = (cols + group_elems - 1) / group_elems;
   const uint64_t last_chunk = (cols - 1) / 512;
   const u32x4* fill = neg_zero_chunk();
+  const uint32_t row_bytes = uint32_t((cols * 2 + 15) & ~uint64_t(15));
   u32x4 keep[R];
   if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
   const uint64_t K = (rows - 1 - g) / T + 1;
@@ -86,7 +90,11 @@ __device__ __forceinline__ void rows_fixed_flat(const uint16_t* __restrict__ x, 
   uint64_t issued = 0;
   const uint16_t* load_row = x + g * ld;
   auto load = [&](u32x4 (&v)[R]) {
-    load_row_chain_counted<R, NT, PARTIAL>(load_row, lc, last_chunk, fill, lane, v);
+    if constexpr (RANGE) {
+      load_row_chain_range<R, NT>(load_row, row_bytes, lc, lane, v);
+    } else {
+      load_row_chain_counted<R, NT, PARTIAL>(load_row, lc, last_chunk, fill, lane, v);
+    }
     // stays on the last streamed item once it is reached (the re-read is not used)
     const bool more = ++issued < items;
     const bool more_in_row = lc + 1 < gpr;
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(1024) void rows_fixed_kernel(const uint16_t* __rest
       const uint64_t g = (remap ? xcd_block_id() : uint64_t(blockIdx.x)) * W + wave_id();
       const uint64_t T = uint64_t(gridDim.x) * W;
       if (cols % (uint64_t(R) * 512) != 0) {
-        rows_fixed_flat<R, NT, MMA, true>(x, rows, cols, ld, out, g, T, lane);
+        rows_fixed_flat<R, NT, MMA, true, true>(x, rows, cols, ld, out, g, T, lane);
       } else {
         rows_fixed_flat<R, NT, MMA, false>(x, rows, cols, ld, out, g, T, lane);
       }

@@ -57,8 +57,10 @@ struct RowCursor {
 // by row_tail_keep).  At the end of a row its total is written and the
 // running sum restarts.
 // PARTIAL: whether rows end inside a chain (instantiated apart, so that whole
-// chains carry no masking code at all).
-template <int R, bool NT, int D, bool PARTIAL>
+// chains carry no masking code at all).  RANGE (with PARTIAL, for rows of
+// less than 2 GiB): the chains are read by load_row_chain_range, so nothing
+// past a row's last 16-byte slot is fetched.
+template <int R, bool NT, int D, bool PARTIAL, bool RANGE = false>
 __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64_t rows,
                                           uint64_t cols, uint64_t ld, float* __restrict__ out,
                                           uint64_t g, uint64_t T, int lane) {
@@ -67,6 +69,7 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
   const uint64_t cpr = (cols + chain_elems - 1) / chain_elems;
   const uint64_t last_chunk = (cols - 1) / 512;
   const u32x4* fill = neg_zero_chunk();
+  const uint32_t row_bytes = uint32_t((cols * 2 + 15) & ~uint64_t(15));
   u32x4 keep[R];
   if constexpr (PARTIAL) row_tail_keep<R>(cols, lane, keep);
   const uint64_t K = (rows - 1 - g) / T + 1;
@@ -75,7 +78,11 @@ __device__ __forceinline__ void rows_flat(const uint16_t* __restrict__ x, uint64
   RowCursor pf, rd, pr;   // next item to load, to reduce, to retire
   const uint16_t* load_row = x + g * ld;
   auto load = [&](u32x4 (&v)[R]) {
-    load_row_chain<R, NT>(load_row, pf.c, last_chunk, fill, lane, v);
+    if constexpr (RANGE) {
+      load_row_chain_range<R, NT>(load_row, row_bytes, pf.c, lane, v);
+    } else {
+      load_row_chain<R, NT>(load_row, pf.c, last_chunk, fill, lane, v);
+    }
     // stays on the last item once it is reached (the re-read is not used)
     if (pf.c + 1 < cpr) {
       ++pf.c;
@@ -264,7 +271,9 @@ __global__ __launch_bounds__(1024) void rows_kernel(const uint16_t* __restrict__
     const uint64_t T = uint64_t(gridDim.x) * W;
     // the last row stays out of the stream when rows end inside a chain
     const uint64_t streamed = tail ? rows - 1 : rows;
-    if (tail) {
+    if (tail && cols < kRowsRangeMaxCols) {
+      rows_flat<R, NT, D, true, true>(x, streamed, cols, ld, out, g, T, lane);
+    } else if (tail) {
       rows_flat<R, NT, D, true>(x, streamed, cols, ld, out, g, T, lane);
     } else {
       rows_flat<R, NT, D, false>(x, streamed, cols, ld, out, g, T, lane);

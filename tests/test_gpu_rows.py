@@ -127,3 +127,22 @@ def test_long_rows_stream(cols):
         got = armx.reduce_rows(xd, **cfg).cpu().numpy()
         check_rows(x, got, f"{rows}x{cols} {cfg}")
 
+
+
+@pytest.mark.parametrize("cols", [601, 1003, 2261, 4005])
+def test_pitch_padding_never_summed(cols):
+    # the row stream reads a row's last lane slot whole and masks the values
+    # past the row; a pitch one slot wider than needed, full of NaN, shows
+    # any value past the row that reaches a sum (601 and 1003: the row ends
+    # inside a lane's 8 values; 2261, 4005 at the default and other chain
+    # lengths: inside a chain, with whole chunks past the row)
+    rows = 2000
+    ld = (cols + 7) // 8 * 8 + 8
+    x = si.generate_rows("normal", rows, cols, seed=cols + 1)
+    pad = np.full((rows, ld), np.nan, np.float16)
+    pad[:, :cols] = x
+    xd = to_dev(pad)[:, :cols]
+    for cfg in [dict(), dict(plain=True), dict(chain_r=4, block_threads=256),
+                dict(chain_r=8, block_threads=64, grid_blocks=32)]:
+        got = armx.reduce_rows(xd, **cfg).cpu().numpy()
+        check_rows(x, got, f"{rows}x{cols} ld {ld} {cfg}")

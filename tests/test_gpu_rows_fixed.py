@@ -115,3 +115,19 @@ def test_full_4096x65536_normal():
     # batch invariance against the flat fixed order on sampled rows
     for r in (0, 1234, 4095):
         assert bits(armx.reduce_sum_fixed_order(xd[r].contiguous()).cpu().numpy())[()] == want[r]
+
+
+@pytest.mark.parametrize("cols", [601, 1003, 2261, 4005])
+def test_pitch_padding_never_summed(cols):
+    # as in the free order: a NaN pitch past each row must not reach a root,
+    # and the zeros of the range-checked loads past the row must act as -0.0
+    rows = 2000
+    ld = (cols + 7) // 8 * 8 + 8
+    x = si.generate_rows("normal", rows, cols, seed=cols + 2)
+    pad = np.full((rows, ld), np.nan, np.float16)
+    pad[:, :cols] = x
+    xd = to_dev(pad)[:, :cols]
+    want = bits(fixed_tree_row_sums(x))
+    for cfg in [dict(), dict(chain_r=1), dict(chain_r=4, block_threads=64, grid_blocks=32)]:
+        got = armx.reduce_rows_fixed_order(xd, **cfg).cpu().numpy()
+        assert np.array_equal(bits(got), want), (cols, cfg)
