@@ -24,13 +24,15 @@
 // That default form uses no MFMA.  ARMX_FLAG_INT_LIMBS selects the form
 // whose sums are integer MFMAs over 8-bit limbs (the limb planes of the AWE
 // Abstract): every value's count q (|q| < 2^40) is written as eight signed
-// 8-bit digits d_0 .. d_7 with q = s + sum_m d_m 2^(8m) (s = 1 for a negative
-// value, else 0; see value_digits), and v_mfma_i32_16x16x64_i8 against a
+// 8-bit digits d_0 .. d_7 (the bytes of its two's complement with their top
+// bits flipped; see value_digits), and v_mfma_i32_16x16x64_i8 against a
 // digit-selector operand adds, per output column, the digits of each
 // position m over 8 values per MFMA -- exact in 32-bit integers -- so the
-// digit planes are summed by the matrix cores and recombined with their
-// weights 2^(8m) at the end.  Building the digits costs about a dozen
-// vector instructions per value, against three for the binary64 form.
+// digit planes are summed by the matrix cores and recombined at the end:
+// positions 0-4 with their weights 2^(8m), plus a constant per value and a
+// term per negative value, whose count position 7 gives.  Building the
+// digits costs about 14 vector instructions per value, against three for
+// the binary64 form.
 //
 // Non-finite inputs: a chain whose binary64 sum is not finite sets a flag
 // (+Inf, -Inf or NaN) instead of adding to the integers; the result follows
@@ -87,24 +89,30 @@ __device__ __forceinline__ void add_chain(const u32x4 (&v)[R], Exact& a) {
 // Digits of one value.  A finite binary16 value is q 2^-24 with q = +-M 2^t,
 // M = the significand with its hidden bit (f, or 1024 + f), t = e - 1 (0 for
 // subnormals, e the exponent field), |q| < 2^40.  Let g = |q| xor (all ones
-// if negative), so g = q for q >= 0 and g = q - 1 for q < 0 (two's
-// complement), and y = g + C with C = 0x8080808080808080.  The bytes y_m of y
-// read as signed 8-bit digits after flipping their top bit, d_m = y_m - 128
-// (y_m xor 0x80 as int8), satisfy sum_m d_m 2^(8m) = y - C; and g + C lies in
-// [0, 2^64) because |g| < 2^40, so y = g + C with no wrap-around and the
-// digits give g exactly: q = s + sum_m d_m 2^(8m) with s = 1 for a negative
-// value.  The eight digits are returned as
-// the bytes of one 64-bit word (digit m in byte m).  An exponent field of 31
-// (infinity, NaN) gives digits of no meaning; such chains are flagged apart.
-__device__ __forceinline__ uint64_t value_digits(uint32_t h) {
-  constexpr uint64_t C = 0x8080808080808080ull;
-  const uint32_t e = (h >> 10) & 31u;
+// if negative): g = q for q >= 0 and g = q - 1 for q < 0, in two's
+// complement.  The digits are the bytes g_m of g with their top bit flipped,
+// read as signed 8-bit integers: d_m = g_m - 128 (in [-128, 127]).  Bytes
+// 0-4 hold g mod 2^40 = q, or 2^40 + q - 1 for a negative value, so
+//   q = sum_{m<5} d_m 2^(8m) + C40 + [q < 0] (1 - 2^40),
+// C40 = 0x8080808080; bytes 5-7 are all 0x00 (d = -128) for q >= 0 and all
+// 0xFF (d = 127) for q < 0, so the sum of digit 7 over N values is
+// 255 #negative - 128 N, which counts the negative values.  The eight
+// digits are returned as the bytes of one 64-bit word (digit m in byte m):
+// the flip and the sign are one xor with (all ones if negative) xor
+// 0x80...80.  An exponent field of 31 (infinity, NaN) gives digits of no
+// meaning; such chains are flagged apart.
+// Half HI (0 or 1) of the 32-bit word w holds the value; `e` receives its
+// exponent field.
+template <int HI>
+__device__ __forceinline__ uint64_t value_digits(uint32_t w, uint32_t& e) {
+  e = (w >> (10 + 16 * HI)) & 31u;
+  const uint32_t f = (w >> (16 * HI)) & 1023u;
+  const int32_t sign = HI ? int32_t(w) >> 31 : int32_t(w << 16) >> 31;   // 0 or -1
   const uint32_t mn = __builtin_elementwise_min(e, 1u);
-  const uint32_t m = (mn << 10) | (h & 1023u);
+  const uint32_t m = (mn << 10) | f;
   const uint64_t mag = uint64_t(m) << (e - mn);
-  const uint32_t s32 = uint32_t(int32_t(h << 16) >> 31);   // 0 or all ones
-  const uint64_t g = mag ^ (uint64_t(s32) << 32 | s32);
-  return (g + C) ^ C;
+  const uint32_t k = uint32_t(sign) ^ 0x80808080u;
+  return mag ^ (uint64_t(k) << 32 | k);
 }
 
 typedef int int4v __attribute__((ext_vector_type(4)));
@@ -129,73 +137,71 @@ __device__ __forceinline__ int4v digit_selector(int lane) {
 // Per-lane state of the limb form: the digit-position sums of this lane's
 // accumulator rows (lane l holds rows 4 (l / 16) .. + 3 of column l % 16:
 // digit positions 0-3 in lanes 0-15, 4-7 in lanes 16-31, zero in lanes
-// 32-63), the count of negative values this lane loaded (the s terms), and
-// the largest exponent field it loaded (31: an infinity or a NaN).
+// 32-63), and the largest exponent field it loaded (31: an infinity or a
+// NaN).
 struct LimbSums {
   int64_t pos[4];
-  uint64_t negatives;
-  uint32_t expo;   // the largest exponent field (bits 10-14) of any value seen
+  uint32_t expo;   // the largest exponent field (0-31) of any value seen
 };
 
 // One chain of R loads (8 R values per lane): 4 R integer MFMAs (two values'
 // digits, 16 bytes, per lane each) into two accumulators in turn (so that
 // consecutive MFMAs do not wait for each other), exact in 32 bits within the
 // chain (8 digits of at most 128 in magnitude per element per MFMA), then
-// added into the 64-bit sums.  Values with exponent field 31 (infinity,
-// NaN) give digits of no meaning; the largest exponent field is kept, and a
-// wavefront that saw 31 works out the non-finite flags after its stream.
+// added into the 64-bit sums.  Every output column takes 8 values per MFMA,
+// 32 per load.  Values with exponent field 31 (infinity, NaN) give digits
+// of no meaning; the largest exponent field is kept, and a wavefront that
+// saw 31 works out the non-finite flags after its stream.
 template <int R>
 __device__ __forceinline__ void add_chain_limbs(const u32x4 (&v)[R], const int4v sel,
                                                 LimbSums& ls) {
   int4v acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
   uint32_t expo = ls.expo;
-  unsigned neg = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
 #pragma unroll
     for (int w = 0; w < 4; w += 2) {
-      const uint64_t d0 = value_digits(v[r][w] & 0xFFFFu);
-      const uint64_t d1 = value_digits(v[r][w] >> 16);
-      const uint64_t d2 = value_digits(v[r][w + 1] & 0xFFFFu);
-      const uint64_t d3 = value_digits(v[r][w + 1] >> 16);
+      uint32_t e0, e1, e2, e3;
+      const uint64_t d0 = value_digits<0>(v[r][w], e0);
+      const uint64_t d1 = value_digits<1>(v[r][w], e1);
+      const uint64_t d2 = value_digits<0>(v[r][w + 1], e2);
+      const uint64_t d3 = value_digits<1>(v[r][w + 1], e3);
       const int4v b01 = {int(uint32_t(d0)), int(uint32_t(d0 >> 32)), int(uint32_t(d1)),
                          int(uint32_t(d1 >> 32))};
       const int4v b23 = {int(uint32_t(d2)), int(uint32_t(d2 >> 32)), int(uint32_t(d3)),
                          int(uint32_t(d3 >> 32))};
       acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sel, b01, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(sel, b23, acc1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      neg += __builtin_popcount(v[r][w] & 0x80008000u);
-      const uint32_t ex = v[r][w] & 0x7C007C00u;
-      const uint32_t lo = ex & 0xFFFFu, hi = ex >> 16;
-      expo = expo > lo ? expo : lo;
-      expo = expo > hi ? expo : hi;
+      expo = __builtin_elementwise_max(expo, __builtin_elementwise_max(e0, e1));
+      expo = __builtin_elementwise_max(expo, __builtin_elementwise_max(e2, e3));
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) ls.pos[r] += int64_t(acc0[r]) + int64_t(acc1[r]);
-  ls.negatives += neg;
   ls.expo = expo;
 }
 
-// The lane's limb sums as an Exact (digit position m weighs 2^(8m)).
-__device__ __forceinline__ void limbs_to_exact(const LimbSums& ls, int lane, Exact& a) {
-  const int base = ((lane >> 4) & 1) * 4;   // lanes 32-63 hold zeros
+// The lane's limb sums as an Exact, after `loads` loads per lane (N = 32
+// loads values per output column): positions 0-4 weigh 2^(8m); the lane of
+// positions 4-7 of a column adds N C40 and, with the column's negative
+// count #neg = (D7 + 128 N) / 255 from its digit-7 sum D7, #neg (1 - 2^40).
+__device__ __forceinline__ void limbs_to_exact(const LimbSums& ls, int lane, uint64_t loads,
+                                               Exact& a) {
+  if ((lane >> 4) & 2) return;   // lanes 32-63 hold zeros
+  if (((lane >> 4) & 1) == 0) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = base + r;
-    const int64_t v = ls.pos[r];
-    if (m < 4) {
-      const int64_t t = int64_t(uint64_t(v) << (8 * m));
+    for (int m = 0; m < 4; ++m) {
+      const int64_t t = int64_t(uint64_t(ls.pos[m]) << (8 * m));
       a.hi += t >> 32;
       a.lo += uint64_t(t) & 0xFFFFFFFFull;
-    } else {
-      a.hi += int64_t(uint64_t(v) << (8 * m - 32));
     }
+  } else {
+    const uint64_t N = 32 * loads;
+    const uint64_t neg = uint64_t(ls.pos[3] + int64_t(128 * N)) / 255u;
+    a.hi += ls.pos[0];                                   // digit 4: 2^32
+    a.hi += int64_t(N * 0x80u) - int64_t(neg << 8);      // N C40 and -#neg 2^40
+    a.lo += N * 0x80808080ull + neg;
   }
-  a.lo += ls.negatives;
 }
 
 // The full chains c0, c0 + stride, ... (`iters` of them), with the load
@@ -423,7 +429,7 @@ __global__ __launch_bounds__(LIMBS ? kExactLimbsMaxBlock : 1024) void exact_kern
   uint64_t c = uint64_t(blockIdx.x) * W + uint64_t(wave_id());
 
   Exact a{0, 0, 0};
-  LimbSums ls{{0, 0, 0, 0}, 0, 0};
+  LimbSums ls{{0, 0, 0, 0}, 0};
   const uint64_t c0 = c;
   const uint64_t iters = c < chains_full ? (chains_full - 1 - c) / total_waves + 1 : 0;
   // No request pacing (pace_pause): the binary64 additions already space a
@@ -451,14 +457,14 @@ __global__ __launch_bounds__(LIMBS ? kExactLimbsMaxBlock : 1024) void exact_kern
     }
   }
   if constexpr (LIMBS) {
-    limbs_to_exact(ls, lane, a);
+    limbs_to_exact(ls, lane, (iters + (tail ? 1 : 0)) * R, a);
     // A wavefront that loaded an infinity or a NaN reads its chains again in
     // binary64 (add_chain) for the non-finite flags only: a set flag decides
     // the result and the integers are then not used.  Never taken on finite
     // data, so the stream above carries no such work.
-    if (__builtin_amdgcn_ballot_w64(ls.expo == 0x7C00u) != 0) {
+    if (__builtin_amdgcn_ballot_w64(ls.expo == 31u) != 0) {
       Exact f{0, 0, 0};
-      LimbSums unused{{0, 0, 0, 0}, 0, 0};
+      LimbSums unused{{0, 0, 0, 0}, 0};
       stream_exact<R, NT, false>(x, c0, iters, total_waves, lane, f, unused);
       if (tail) {
         u32x4 v[R];

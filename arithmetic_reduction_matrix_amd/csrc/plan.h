@@ -45,11 +45,12 @@ constexpr size_t kExactRecordBytes = 32;
 // its digit words need more registers than a 1024-thread block leaves a lane;
 // a larger requested block is lowered to this.
 constexpr int kExactLimbsMaxBlock = 512;
-// Its defaults: about 16 vector instructions per value make it bound by the
+// Its defaults: about 14 vector instructions per value make it bound by the
 // vector ALUs, which want every SIMD busy -- measured on MI355X at 2^28 values
-// (us): blocks of 512 at R = 8 (8 wavefronts per CU) 125.5, R = 4 127.3,
-// R = 2 135.1; blocks of 128 at R = 8 (2 per CU) 251.9.
-constexpr OpDefaults kExactLimbsDefaults{512, 8, 16};
+// (us, events around 50 calls, two copies in turn): blocks of 512 at R = 4
+// (8 wavefronts per CU) 111.9, R = 2 117.7, R = 8 137.9; blocks of 256 at
+// R = 4 114.1, R = 8 116.7; blocks of 128 at R = 8 (2 per CU) 212.2.
+constexpr OpDefaults kExactLimbsDefaults{512, 4, 16};
 // The fixed-order final combine handles at most this many block results.
 constexpr int kFixedMaxBlocks = 4096;
 // Largest fixed-order per-wave chunk count is 2^kFixedMaxLog2Chunks.

@@ -116,7 +116,7 @@ typedef struct armx_config {
 /* Defaults (block_threads, chain_r), measured on MI355X:
  *   reduce_sum 128, 8; reduce_sum_fixed_order 128, 8; reduce_rows 64, 8;
  *   reduce_rows_fixed_order 64, 4; reduce_sum with ARMX_FLAG_MMA_LEVELS
- *   256, 8; reduce_sum_exact 128, 8 (with ARMX_FLAG_INT_LIMBS 512, 8, and
+ *   256, 8; reduce_sum_exact 128, 8 (with ARMX_FLAG_INT_LIMBS 512, 4, and
  *   larger blocks lowered to 512).
  * Automatic persistent grids hold about 16 / R wavefronts per compute unit
  * (2 at the default R: fewer, deeper load streams reach more HBM bandwidth;
@@ -342,10 +342,10 @@ int reduce_rows_fixed_order(const void* x, size_t rows, size_t cols, size_t ld, 
  * weights 2^(8m)), and v_mfma_i32_16x16x64_i8 against a digit-selector
  * operand sums each digit position exactly in 32-bit integers -- the integer
  * matrix cores do the additions -- before the positions are recombined with
- * their weights; same result bits, but about 16 vector instructions per
+ * their weights; same result bits, but about 14 vector instructions per
  * value to form the digits against 3 for the binary64 form, so it is bound
- * by the vector ALUs (measured on MI355X at 2^28 values: 125 us against
- * 77 us); the binary64 form is the default for that reason.
+ * by the vector ALUs (measured on MI355X at 2^28 values: about 112 us
+ * against 77 us); the binary64 form is the default for that reason.
  * Returns ARMX_OK or ARMX_ERR_{NULL,ALIGN,CONFIG,WORKSPACE,SHAPE,HIP}.
  */
 int reduce_sum_exact(const void* x, size_t n, float* out, int64_t* out_fixed, void* ws,
