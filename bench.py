@@ -415,6 +415,7 @@ def main() -> int:
         "result": result,
     }
 
+    print(f"bench: headline done, {avg_ms * 1e3:.2f} us per launch", file=sys.stderr, flush=True)
     # ---- the achievable read rate on this device -------------------------------
     if not args.no_read_ceiling:
         ceil_gbs, ceil_cfg = read_ceiling(torch, bufs, n, props.multi_processor_count)
@@ -425,6 +426,7 @@ def main() -> int:
             "best_shape": ceil_cfg,
         }
 
+    print("bench: read ceiling done", file=sys.stderr, flush=True)
     # ---- the other rows of the hot path ---------------------------------------
     stress_np = None   # the 2^30 precision-stress input, drawn with the variants
     if not args.no_variants:
@@ -684,6 +686,7 @@ def main() -> int:
             print(f"n=2^{k}", json.dumps(row), file=sys.stderr, flush=True)
         record["levels_sweep"] = lv
 
+    print("bench: variants done", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         xf_cpu = si.workload("fixed_2p26_u11")
         record["cpu_baseline"], e, e30, tree26 = cpu_baseline(x_np, xf_cpu, stress_np=stress_np)
