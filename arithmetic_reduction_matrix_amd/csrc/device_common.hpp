@@ -473,11 +473,12 @@ __device__ __forceinline__ float load_published(const float* slot) {
 // index order, padded with -0.0 to P, the power of two at or above S.  For
 // P <= 64 a group of P lanes takes a row (64 / P rows per wavefront at a
 // time); above, a wavefront takes a row with k = P / 64 parts per lane (at
-// most 8), added pairwise in registers first.  Called by every thread.
+// most 8), added pairwise in registers first.  Called by every thread of a
+// block of `nt` threads (the size as read at the start of the kernel: read
+// after the ticket it costs a memory round trip).
 __device__ inline void combine_split_rows(const float* parts, uint64_t rows, unsigned S,
-                                          float* __restrict__ out, float* stage) {
+                                          float* __restrict__ out, float* stage, unsigned nt) {
   const uint64_t items = rows * S;
-  const uint64_t nt = blockDim.x;
   for (uint64_t base = threadIdx.x; base < items; base += 8 * nt) {
     float v[8];
 #pragma unroll
@@ -495,7 +496,7 @@ __device__ inline void combine_split_rows(const float* parts, uint64_t rows, uns
   int lp = 0;
   while ((1u << lp) < S) ++lp;
   const int lane = lane_id();
-  const uint64_t W = uint64_t(num_waves());
+  const uint64_t W = uint64_t(nt) / 64;
   if (lp <= 6) {
     const uint64_t P = uint64_t(1) << lp, per_wave = uint64_t(64) >> lp;
     for (uint64_t r0 = uint64_t(wave_id()) * per_wave; r0 < rows; r0 += W * per_wave) {

@@ -88,15 +88,16 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
     return;
   }
   // groups are aligned power-of-two runs of blocks: complete subtrees
+  const unsigned T = unsigned(W) * 64;
   finish_two_level(block_root, counters, roots, group_roots, group, out, red, &flag,
-                   tree_of_values);
+                   [T](const float* v, unsigned c, float* r) { return tree_of_values(v, c, r, T); });
 }
 
 __global__ __launch_bounds__(1024) void fixed_final_kernel(const float* __restrict__ roots,
                                                            unsigned count,
                                                            float* __restrict__ out) {
   __shared__ float red[16];
-  const float root = tree_of_values(roots, count, red);
+  const float root = tree_of_values(roots, count, red, blockDim.x);
   if (threadIdx.x == 0) out[0] = root;
 }
 

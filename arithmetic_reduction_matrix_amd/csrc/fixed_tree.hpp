@@ -156,11 +156,14 @@ __device__ __forceinline__ float counter_fold(const float (&stk)[kStack], uint64
 }
 
 // Balanced tree over `count` values (padded with -0.0 to a power of two) with
-// one block whose size is a power of two; result valid in thread 0.
-__device__ inline float tree_of_values(const float* vals, unsigned count, float* red) {
+// one block of T threads, T a power of two; result valid in thread 0.  The
+// caller passes T as read at the start of its kernel: read here, after a
+// completion ticket's atomics and fences, the block size is fetched from
+// memory again (a round trip on the last block's path).
+__device__ inline float tree_of_values(const float* vals, unsigned count, float* red,
+                                       unsigned T) {
   unsigned p2 = 1;
   while (p2 < count) p2 <<= 1;
-  const unsigned T = blockDim.x;
   const unsigned used = p2 < T ? p2 : T;   // threads with leaves
   const unsigned per = p2 / used;          // consecutive leaves per thread
   const unsigned t = threadIdx.x;

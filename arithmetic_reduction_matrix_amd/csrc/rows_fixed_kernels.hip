@@ -223,7 +223,7 @@ __global__ __launch_bounds__(1024) void rows_fixed_split_kernel(
   }
   __syncthreads();   // every wavefront's root is stored before the block counts
   if (!publish_with_ticket([] {}, counter, gridDim.x, &flag)) return;
-  combine_split_rows(partials, rows, segs, out, stage);
+  combine_split_rows(partials, rows, segs, out, stage, unsigned(W) * 64);
 }
 
 template <int R>

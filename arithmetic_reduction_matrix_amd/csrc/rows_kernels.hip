@@ -341,7 +341,7 @@ __global__ __launch_bounds__(1024) void rows_split_kernel(const uint16_t* __rest
   }
   __syncthreads();   // every wavefront's partial is stored before the block counts
   if (!publish_with_ticket([] {}, counter, gridDim.x, &flag)) return;
-  combine_split_rows(partials, rows, segs, out, stage);
+  combine_split_rows(partials, rows, segs, out, stage, unsigned(W) * 64);
 }
 
 template <template <int, bool, int> class K, int R, bool NT>
