@@ -144,10 +144,13 @@ int reduce_sum_noalloc(const void* x, size_t n, float* out, const armx_config* c
   if (plan.ws_bytes > 0) {
     if (armx::scratch_address(&ws) != hipSuccess) return ARMX_ERR_HIP;
     // the completion counters the plan uses (the top counter and one per
-    // group, each kCounterStride words apart) must start at zero: cleared by
-    // a small kernel on the caller's stream (capturable; no memset, no
-    // allocation)
-    const uint64_t groups = plan.group ? (uint64_t(plan.grid) + plan.group - 1) / plan.group : 0;
+    // group, each kCounterStride words apart; with one group, one per run of
+    // kSplitCountRun blocks when the kernel splits its counting) must start
+    // at zero: cleared by a small kernel on the caller's stream (capturable;
+    // no memset, no allocation)
+    uint64_t groups = plan.group ? (uint64_t(plan.grid) + plan.group - 1) / plan.group : 0;
+    if (groups == 1)
+      groups = (uint64_t(plan.grid) + armx::kSplitCountRun - 1) / armx::kSplitCountRun;
     const uint64_t words = (1 + groups) * armx::kCounterStride;
     const hipError_t e = armx::launch_zero(
         static_cast<float*>(ws),

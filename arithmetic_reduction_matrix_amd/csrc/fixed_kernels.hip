@@ -90,7 +90,8 @@ __global__ __launch_bounds__(1024) void fixed_kernel(const u32x4* __restrict__ x
   // groups are aligned power-of-two runs of blocks: complete subtrees
   const unsigned T = unsigned(W) * 64;
   finish_two_level(block_root, counters, roots, group_roots, group, out, red, &flag,
-                   [T](const float* v, unsigned c, float* r) { return tree_of_values(v, c, r, T); });
+                   [T](const float* v, unsigned c, float* r) { return tree_of_values(v, c, r, T); },
+                   span < kSplitCountChains * R);
 }
 
 __global__ __launch_bounds__(1024) void fixed_final_kernel(const float* __restrict__ roots,

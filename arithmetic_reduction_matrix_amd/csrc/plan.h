@@ -65,6 +65,9 @@ constexpr size_t kFixedLdsBytes = 64 * 1024;
 // at R = 5: 1105 us with the 64 counters packed in 256 bytes, 187 us spread,
 // 99 us spread with up to 255 groups).
 constexpr unsigned kCounterStride = 64;
+// A single ticket group whose blocks may split their counting (short
+// streams) counts them in runs of this many blocks, one counter per run.
+constexpr unsigned kSplitCountRun = 16;
 constexpr unsigned kMaxGroups = 255;
 constexpr size_t kCounterBytes = size_t(1 + kMaxGroups) * kCounterStride * sizeof(unsigned);
 static_assert(kCounterBytes == ARMX_COUNTER_BYTES, "the header's counter region size");

@@ -41,7 +41,8 @@ namespace {
 
 using namespace dev;
 
-static_assert(kTicketGroups == kMaxGroups && kTicketStride == kCounterStride,
+static_assert(kTicketGroups == kMaxGroups && kTicketStride == kCounterStride &&
+                  dev::kSplitCountRun == armx::kSplitCountRun,
               "the kernels' ticket layout is the plan's workspace layout");
 
 // Reduces partials[0..count) in a fixed order with one block; valid in thread 0.
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(1024) void sum_kernel(const u32x4* __restrict__ x, 
     return;
   }
   finish_two_level(block_total, counters, partials, group_partials, group, out, red, &flag,
-                   reduce_partials);
+                   reduce_partials, chains_full < kSplitCountChains * total_waves);
 }
 
 __global__ __launch_bounds__(1024) void final_sum_kernel(const float* __restrict__ partials,
