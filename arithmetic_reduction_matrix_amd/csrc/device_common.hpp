@@ -541,19 +541,21 @@ constexpr unsigned kTicketGroups = 255;
 constexpr unsigned kTicketStride = 64;
 
 //
-// With one group of more than 16 blocks and `split_count` (short streams, so
-// that every block arrives at about the same time), only the counting is
-// split: each run of 16 blocks has a counter, the last of each run counts
+// With one group of at least kSplitCountMinBlocks blocks and `split_count`
+// (short streams, so that every block arrives at about the same time), only
+// the counting is split: each run of 16 blocks has a counter, the last of each run counts
 // on the top counter, and the last of those combines all the block results
 // at once.  Measured on MI355X (256 blocks, graph-timed): at 2^24 values the
 // free-order sum 9.65-9.95 -> 8.67-8.79 us and the fixed order 10.93 ->
 // 10.02 us, since 256 increments of one counter, arriving together, are
 // served one after another; at 2^26 and 2^28 the streams end spread out and
-// the extra round trip costs 0.3-0.5 us, so longer streams keep one counter.
+// the extra round trip costs 0.3-0.5 us, so longer streams keep one counter,
+// and so do grids of fewer blocks (2^20 values, 64 blocks: 4.20 -> 4.57 us).
 // Streams of fewer than kSplitCountChains chains (or fixed-order groups) per
 // wavefront split their counting, in runs of kSplitCountRun blocks.
 constexpr uint64_t kSplitCountChains = 16;
 constexpr unsigned kSplitCountRun = 16;
+constexpr unsigned kSplitCountMinBlocks = 128;
 
 template <class Combine>
 __device__ __forceinline__ void finish_two_level(float value, unsigned* counters,
@@ -565,7 +567,7 @@ __device__ __forceinline__ void finish_two_level(float value, unsigned* counters
   const unsigned g = b / group, g0 = g * group;
   const unsigned in_group = G - g0 < group ? G - g0 : group;
   const unsigned groups = (G + group - 1) / group;
-  if (split_count && groups == 1 && G > kSplitCountRun) {
+  if (split_count && groups == 1 && G >= kSplitCountMinBlocks) {
     const unsigned runs = (G + kSplitCountRun - 1) / kSplitCountRun, s = b / kSplitCountRun;
     const unsigned in_run = G - s * kSplitCountRun < kSplitCountRun ? G - s * kSplitCountRun
                                                                     : kSplitCountRun;
